@@ -1,0 +1,268 @@
+"""ExpCast FP8 attention, step by step, in float64 on the CPU.
+
+TEST INFRASTRUCTURE ONLY: only tests/, the smoke check and the benchmark's CPU
+baseline may import this module; the GPU library shares no code with it.
+
+Sources (the pages this follows):
+  * Open VC Attention product page (ailibri.com), API paragraph: multi-head
+    forward attention, head dim 128, FP16/BF16 inputs [B,S,H,128], the call
+    quantizes to FP8 itself and returns BF16.
+  * same page, kernel paragraph: softmax weights are written to FP8 straight
+    from the scores; Q and K carry per-block scales, V a per-head scale; keys
+    are visited from the middle of the window.
+  * VC-Attention write-up (Nunchux AI), section "ExpCast-FP8": an E4M3 byte
+    read as an integer is about 8*log2(v)+56, so the byte is produced from the
+    log-domain score with one fused multiply-add; beta = -0.35 centres the
+    rounding error; the result equals the exp-then-cast byte on 79.6% of
+    entries and is otherwise one code away; per-row total variation < 3.64%
+    plus any underflow tail.
+  * Open-VC news (aikraft.ru), section "Решение: ExpCast и отказ от экспонент",
+    and the product page, repair paragraph: V-residual repair adds back the
+    quantized residual of the worst-rounded value tokens, chosen by residual
+    energy, with a token budget (0.005 in the example).
+
+Readings where the pages leave a step open (each is listed in the design doc):
+  * weights are stored as 256*p, p = 2^(x - M) relative to the row max, so the
+    code is 8*(x - M) + 120 + beta; the largest weight lands on code 120.
+  * the byte is the round-to-nearest-even of that affine value, clamped to the
+    finite codes [0, 126]; keys beyond S get no code.
+  * M is the bit-aligned row max: M = ceil(max_j x_j), an integer.
+  * the row sum is over the decoded weights: L = sum_j dec(c_j).
+  * Q/K scale blocks are 128 tokens x 128 channels; scale s = amax/448 in fp32,
+    quantization multiplies by the fp32 reciprocal 448/amax; an all-zero
+    block gets s = 1.
+  * repair: residual r = v - sv*dec(v_hat) in fp32; energy = sum over the 128
+    channels of r^2 accumulated in float64 in channel order; the top
+    k = ceil(budget*S) tokens by energy (ties to the lower index) are repaired
+    with an E4M3 residual carrying its own per-head scale; the row sums L are
+    left unchanged. The budget is a float64 fraction of the tokens.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from .e4m3 import VALUES, decode, encode
+
+BETA = -0.35
+CODE_OF_PMAX = 120.0     # E4M3 code of 256 = 2^8 (8*8 + 56): where a weight of 1 lands
+QK_BLOCK = 128
+LOG2E = 1.0 / math.log(2.0)
+F32 = np.float32
+
+
+def quant_scale(amax: float):
+    """fp32 dequantization scale s = amax/448 and quantization multiplier
+    inv = 448/amax, both correctly rounded fp32 divisions. amax == 0 -> (1, 1)."""
+    a = F32(amax)
+    if a == 0:
+        return F32(1.0), F32(1.0)
+    return F32(a / F32(448.0)), F32(F32(448.0) / a)
+
+
+def quantize_with(x: np.ndarray, inv) -> np.ndarray:
+    """E4M3 codes of fp32(x * inv) (x must be exact in fp32)."""
+    y = x.astype(F32) * F32(inv)               # fp32 product, round to nearest even
+    return encode(y.astype(np.float64))
+
+
+def quantize_blocks(x: np.ndarray, block: int = QK_BLOCK):
+    """Per-block quantization of one head's [S, 128] tensor: one scale per
+    `block` consecutive tokens (over all 128 channels)."""
+    S = x.shape[0]
+    nblk = (S + block - 1) // block
+    codes = np.empty(x.shape, dtype=np.uint8)
+    scales = np.empty(nblk, dtype=F32)
+    for i in range(nblk):
+        sl = slice(i * block, min(S, (i + 1) * block))
+        s, inv = quant_scale(np.abs(x[sl]).max())
+        scales[i] = s
+        codes[sl] = quantize_with(x[sl], inv)
+    return codes, scales
+
+
+def quantize_head(x: np.ndarray):
+    """One scale for the whole head's [S, 128] tensor."""
+    s, inv = quant_scale(np.abs(x).max())
+    return quantize_with(x, inv), s
+
+
+@dataclass
+class RepairSet:
+    k: int
+    sel: np.ndarray          # selected token indices, ascending
+    energy: np.ndarray       # float64 residual energy of every token
+    rc: np.ndarray           # E4M3 codes of the selected residuals [k, 128]
+    sr: np.float32           # residual dequantization scale
+
+
+@dataclass
+class PreparedHead:
+    qc: np.ndarray
+    sq: np.ndarray           # per 128-token block
+    kc: np.ndarray
+    sk: np.ndarray
+    vc: np.ndarray
+    sv: np.float32
+    repair: RepairSet | None = field(default=None)
+
+    @property
+    def S(self):
+        return self.kc.shape[0]
+
+
+def repair_count(budget: float, S: int) -> int:
+    """k = ceil(budget * S) in float64, with a 1e-9 allowance so that a budget
+    such as 0.05 of 600 tokens gives 30 despite binary rounding; capped at S."""
+    b = float(budget)
+    if not (0.0 <= b <= 1.0):
+        raise ValueError("budget must lie in [0, 1]")
+    return max(0, min(S, int(math.ceil(b * S - 1e-9))))
+
+
+def repair_select(v: np.ndarray, vc: np.ndarray, sv, budget: float) -> RepairSet:
+    """Rank value tokens by the energy of their quantization residual and
+    quantize the residual of the top-k tokens."""
+    S = v.shape[0]
+    k = repair_count(budget, S)
+    t = F32(sv) * decode(vc).astype(F32)       # fp32 product sv*dec(v_hat)
+    r = v.astype(F32) - t                      # fp32 residual
+    energy = np.cumsum(r.astype(np.float64) ** 2, axis=1)[:, -1]   # channel order
+    order = np.lexsort((np.arange(S), -energy))  # energy descending, then index ascending
+    sel = np.sort(order[:k])
+    if k == 0:
+        return RepairSet(0, sel, energy, np.zeros((0, v.shape[1]), np.uint8), F32(1.0))
+    rs = r[sel]
+    sr, inv = quant_scale(np.abs(rs).max())
+    return RepairSet(k, sel, energy, quantize_with(rs, inv), sr)
+
+
+def prepare_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, budget: float = 0.0) -> PreparedHead:
+    """Quantize one (batch, head) slice; inputs are float64 [S, 128] holding
+    bf16/fp16-exact values."""
+    qc, sq = quantize_blocks(q)
+    kc, sk = quantize_blocks(k)
+    vc, sv = quantize_head(v)
+    rep = repair_select(v, vc, sv, budget) if budget > 0 else None
+    return PreparedHead(qc, sq, kc, sk, vc, sv, rep)
+
+
+def log2_logits(ph: PreparedHead, rows, tau: float) -> np.ndarray:
+    """x_ij = tau*log2(e) * sq(i)*sk(j) * <dec(q_hat_i), dec(k_hat_j)> for the
+    given query rows against every key. The dot products of decoded E4M3
+    values are exact in float64 (each product has at most 8 significant bits
+    between 2^-18 and 2^18, so every partial sum of 128 fits in 53 bits)."""
+    rows = np.asarray(rows)
+    qd = decode(ph.qc[rows])
+    kd = decode(ph.kc)
+    dots = qd @ kd.T
+    sqr = ph.sq[rows // QK_BLOCK].astype(np.float64)
+    skk = ph.sk[np.arange(ph.S) // QK_BLOCK].astype(np.float64)
+    return (tau * LOG2E) * dots * (sqr[:, None] * skk[None, :])
+
+
+def bitaligned_row_max(x: np.ndarray) -> np.ndarray:
+    """M_i = ceil(max_j x_ij) as an integer."""
+    return np.ceil(x.max(axis=1)).astype(np.int64)
+
+
+def expcast_codes(x: np.ndarray, M, beta: float = BETA) -> np.ndarray:
+    """ExpCast byte: round-to-nearest-even of 8*(x - M) + 120 + beta, clamped
+    to the finite E4M3 codes [0, 126]."""
+    M = np.asarray(M, dtype=np.float64)
+    if M.ndim == 1:
+        M = M[:, None]
+    y = 8.0 * (x - M) + CODE_OF_PMAX + beta
+    return np.clip(np.rint(y), 0, 126).astype(np.uint8)
+
+
+def exp_cast_codes(x: np.ndarray, M) -> np.ndarray:
+    """The path ExpCast replaces: weight 256*2^(x-M) computed in fp32, then
+    cast to E4M3 with round-to-nearest-even."""
+    M = np.asarray(M, dtype=np.float64)
+    if M.ndim == 1:
+        M = M[:, None]
+    w = np.exp2(x - M + 8.0).astype(F32).astype(np.float64)
+    return encode(w)
+
+
+def expcast_attention_head(q, k, v, tau=None, rows=None, budget=0.0, ph=None,
+                           quantize=True, weights="expcast", chunk=512):
+    """Output rows of ExpCast attention for one (batch, head) slice.
+
+    q, k, v: float64 [S, 128]. Returns a dict with the float64 output rows
+    `out`, the row maxima `M`, row sums `L` and the prepared head `ph`.
+
+    quantize=False skips the FP8 codec (unit scales, raw values);
+    weights="exp" uses the exact weights 2^(x - M) instead of ExpCast bytes.
+    With both switched off the result is textbook softmax attention.
+    """
+    S, D = k.shape
+    tau = 1.0 / math.sqrt(D) if tau is None else tau
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    if ph is None:
+        if quantize:
+            ph = prepare_head(q, k, v, budget)
+        else:
+            ones = lambda n: np.ones(n, dtype=F32)  # noqa: E731
+            ph = PreparedHead(None, ones((S + QK_BLOCK - 1) // QK_BLOCK), None,
+                              ones((S + QK_BLOCK - 1) // QK_BLOCK), None, F32(1.0))
+    vd = decode(ph.vc) if quantize else v
+    out = np.empty((len(rows), D))
+    Ms = np.empty(len(rows), dtype=np.int64)
+    Ls = np.empty(len(rows))
+    for c0 in range(0, len(rows), chunk):
+        r = rows[c0:c0 + chunk]
+        if quantize:
+            x = log2_logits(ph, r, tau)
+        else:
+            x = (tau * LOG2E) * (q[r] @ k.T)
+        M = bitaligned_row_max(x)
+        if weights == "expcast":
+            P = VALUES[expcast_codes(x, M)]
+        elif weights == "exp":
+            P = np.exp2(x - M[:, None])
+        else:
+            raise ValueError(weights)
+        L = P.sum(axis=1)
+        acc = float(ph.sv) * (P @ vd)
+        if quantize and ph.repair is not None and ph.repair.k > 0:
+            rp = ph.repair
+            acc += float(rp.sr) * (P[:, rp.sel] @ decode(rp.rc))
+        out[c0:c0 + len(r)] = acc / L[:, None]
+        Ms[c0:c0 + len(r)] = M
+        Ls[c0:c0 + len(r)] = L
+    return {"out": out, "M": Ms, "L": Ls, "ph": ph}
+
+
+def exact_attention_head(q, k, v, tau=None, rows=None, chunk=512):
+    """softmax(tau * q k^T) v in float64 on the unquantized inputs."""
+    S, D = k.shape
+    tau = 1.0 / math.sqrt(D) if tau is None else tau
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    out = np.empty((len(rows), D))
+    for c0 in range(0, len(rows), chunk):
+        r = rows[c0:c0 + chunk]
+        s = tau * (q[r] @ k.T)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        out[c0:c0 + len(r)] = (p @ v) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+def row_total_variation(codes: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """Per row, half the L1 distance between the normalized decoded weights
+    and the exact softmax of the same (quantized) logits."""
+    P = VALUES[codes]
+    P = P / P.sum(axis=1, keepdims=True)
+    p = np.exp2(x - x.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)
+    return 0.5 * np.abs(P - p).sum(axis=1)
+
+
+def rel_l2(a, b) -> float:
+    """Frobenius-norm relative error ||a - b|| / ||b||."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
