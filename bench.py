@@ -1,0 +1,208 @@
+"""Benchmark of ExpCast FP8 attention on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload s73397_h56] [--budget B]
+
+A step is one full call (FP8 prepare + ExpCast attention; V-residual repair
+when --budget > 0) on inputs already resident in HBM. The last stdout line
+is one JSON record:
+  value        whole-call throughput in TFLOP/s, FLOPs = 4*B*S^2*H*D
+  ms_per_step  milliseconds per full call
+  roofline     the attention kernel against the dense FP8 MFMA peak
+               (5.0 PFLOP/s); its duration comes from HIP events recorded on the
+               stream the kernel is launched on, over --steps kernel-only calls
+  cpu_baseline the CPU oracle (float64 numpy) timed on a bounded sample of the
+               same workload on this host's cores
+plus the prepare time, the repaired call, and a BF16 attention run through
+torch's SDPA on the same GPU for comparison. Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+# HBM bytes per launch of the attention kernel measured with rocprofv3 PMC
+# counters (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration
+# factor) on the headline workload; None until measured for the current kernel.
+MEASURED_TRAFFIC_BYTES = None
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def timed_calls(fn, steps, warmup):
+    """(mean ms per call from HIP events on the current stream, wall ms per call)"""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return float(np.mean([a.elapsed_time(b) for a, b in ev])), wall
+
+
+def cpu_baseline(q, k, v, w, rows_n):
+    """Oracle on one head: quantize all tokens of that head, then ExpCast
+    attention for rows_n sampled query rows against all keys."""
+    import oracle
+    ncores = len(os.sched_getaffinity(0))
+    torch.set_num_threads(ncores)
+    qh, kh, vh = (t[0, :, 0].double().cpu().numpy() for t in (q, k, v))
+    rows = np.array(workloads.sample_rows(w.S, rows_n, seed=w.seed))
+    t0 = time.perf_counter()
+    oracle.expcast_attention_online(qh, kh, vh, rows=rows)
+    t = time.perf_counter() - t0
+    flop = 4.0 * len(rows) * w.S * 128
+    return {"value": flop / t / 1e12, "unit": "TFLOP/s", "cores": ncores, "kind": "oracle",
+            "sample": f"batch 0, head 0 of {w.name}: FP8 prepare of all {w.S} tokens + {len(rows)} query rows "
+                      f"against all keys; {t:.1f} s; FLOPs counted 4*rows*S*D",
+            "seconds": t}
+
+
+def bf16_comparator(q, k, v, steps):
+    """torch SDPA on BF16 [B,H,S,D] tensors (flash / memory-efficient backends
+    only; the math backend would materialize S x S)."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    qt, kt, vt = (x.to(torch.bfloat16).transpose(1, 2).contiguous() for x in (q, k, v))
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+            fn = lambda: torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)  # noqa: E731
+            ms, _ = timed_calls(fn, steps, 1)
+        return ms
+    except Exception as e:  # no fused BF16 backend for this shape
+        log(f"bf16 comparator unavailable: {e}")
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default=workloads.HEADLINE, choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--budget", type=float, default=0.0, help="V-repair budget of the timed full call")
+    ap.add_argument("--repair-budget", type=float, default=0.005, help="budget of the extra repaired measurement")
+    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-comparator", action="store_true")
+    ap.add_argument("--kernel-only", action="store_true", help="time only the attention kernel (for profiling)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the path has no multi-GPU mode (heads would shard with no "
+              "communication; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import bit_fp8_attention_block_amd as oc
+
+    w = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] workload {w.name}: B={w.B} S={w.S} H={w.H} {w.dtype}; generating inputs")
+    q, k, v = workloads.make_inputs(w, device=dev)
+    torch.cuda.synchronize()
+    flop = oc.flops(w.B, w.S, w.H)
+
+    # kernel alone on a prepared workspace (the roofline kernel)
+    prep = oc.prepare_v_repair(q, k, v, max(args.budget, args.repair_budget))
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    log("[bench] attention kernel alone")
+    k_ms, _ = timed_calls(lambda: oc.attention_prepared(prep, with_repair=False, out=out), args.steps, args.warmup)
+    if args.kernel_only:
+        print(json.dumps({"kernel_ms": k_ms, "kernel_tflops": flop / k_ms / 1e9}))
+        return
+    kr_ms, _ = timed_calls(lambda: oc.attention_prepared(prep, with_repair=True, out=out), args.steps, 1)
+    del prep
+
+    # full call (prepare graph + attention), the headline step
+    log("[bench] full call")
+    if args.budget > 0:
+        step = lambda: oc.attention_v_repair(q, k, v, args.budget, out=out)  # noqa: E731
+    else:
+        step = lambda: oc.attention(q, k, v, out=out)  # noqa: E731
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    full_ev_ms, _ = timed_calls(step, args.steps, 0)
+
+    log("[bench] repaired full call")
+    rep_ms, _ = timed_calls(lambda: oc.attention_v_repair(q, k, v, args.repair_budget, out=out), args.steps, 1)
+    # prepare alone (the captured graph), HBM-bound
+    plan = oc.get_plan(q, None, 0.0)
+    ws = oc._workspace(plan, dev)
+    st = lambda: oc._lib.oc_attn_prepare(plan.handle, oc._ptr(q), oc._ptr(k), oc._ptr(v), oc._ptr(ws),  # noqa: E731
+                                         ws.numel(), oc._stream(dev))
+    p_ms, _ = timed_calls(st, args.steps, 1)
+    in_bytes = 3 * 2 * w.B * w.S * w.H * 128
+    prep_bytes = in_bytes + in_bytes // 2 + (in_bytes // 3)   # read q,k,v + V again; write 3 FP8 tensors
+    sdpa_ms = None if args.no_comparator else bf16_comparator(q, k, v, max(2, min(args.steps, 3)))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        cpu = cpu_baseline(q, k, v, w, args.cpu_rows)
+
+    kernel_tflops = flop / k_ms / 1e9
+    # algorithmic bytes of one attention launch: Q, K, V codes read once, BF16 output written once
+    alg_bytes = w.B * w.H * w.S * 128 * 3 + w.B * w.S * w.H * 128 * 2
+    rec = {
+        "metric": "FP8 attn TFLOP/s + ms/call at S=73397,H=56,D=128; % of FP8 MFMA peak",
+        "value": round(flop / ms_per_step / 1e9, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (bf16/fp16 in, bf16 out, fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "S": w.S, "H": w.H, "D": 128, "causal": False,
+                   "input_dtype": str(w.dtype).replace("torch.", ""), "repair_budget": args.budget},
+        "roofline": {"bound": "mfma", "achieved": round(kernel_tflops, 2), "peak": FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(kernel_tflops / FP8_PEAK_TFLOPS, 4),
+                     "traffic": MEASURED_TRAFFIC_BYTES, "kernel": "attn_kernel",
+                     "algorithmic_bytes": alg_bytes},
+        "cpu_baseline": None if cpu is None else {k_: cpu[k_] for k_ in ("value", "unit", "cores", "kind", "sample")},
+        "kernel_ms": round(k_ms, 4),
+        "kernel_tflops": round(kernel_tflops, 2),
+        "kernel_repair_ms": round(kr_ms, 4),
+        "full_call_ms_events": round(full_ev_ms, 4),
+        "prepare_ms": round(p_ms, 4),
+        "prepare_gbs": round(prep_bytes / p_ms / 1e6, 1),
+        "full_call_repair_ms": round(rep_ms, 4),
+        "repair_budget_measured": args.repair_budget,
+        "bf16_sdpa_ms": None if sdpa_ms is None else round(sdpa_ms, 3),
+        "speedup_vs_bf16_sdpa": None if sdpa_ms is None else round(sdpa_ms / ms_per_step, 3),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,264 @@
+"""ExpCast FP8 forward attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over liboc_attn.so (C ABI in include/oc_attn.h).
+PyTorch is used only to hold device memory and name the stream. Every
+step of the computation runs in the library's HIP kernels, and there is no
+fallback path: if the library is missing, importing the binding raises.
+
+    out = attention(q, k, v)                     # full call: prepare + attention
+    prep = prepare_v_repair(q, k, v, 0.005)      # quantize + pick repair tokens
+    out = attention_v_repair(q, k, v, 0.005)     # full call with V-residual repair
+    out = attention_prepared(prep, with_repair=True)   # attention on a prepared workspace
+
+q, k, v: CUDA (HIP) tensors [B,S,H,128] or [S,H,128] in bf16 or fp16, with a
+contiguous channel dimension and 16-byte aligned rows. The output is bf16
+[B,S,H,128] (or [S,H,128]).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboc_attn.so")
+
+OC_OK, OC_ERR_INVALID_ARGUMENT, OC_ERR_UNSUPPORTED, OC_ERR_WORKSPACE_TOO_SMALL, OC_ERR_NOT_PREPARED, OC_ERR_HIP = range(6)
+OC_BF16, OC_FP16 = 0, 1
+
+
+class OcAttnError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(msg)
+        self.status = status
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("S", ctypes.c_int32), ("H", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("stride_b", ctypes.c_int64), ("stride_s", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64), ("softmax_scale", ctypes.c_float)]
+
+
+class WsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in ("qhat", "kpack", "vpack", "sq", "sk", "vamax", "sv", "energy", "sel",
+                                               "kselpack", "rpack", "sksel", "sr", "total_bytes")] + \
+               [(n, ctypes.c_int32) for n in ("n_ktiles", "n_qtiles", "s_pad_q", "n_sel_max", "n_sel_tiles_max")]
+
+
+EXPORTS = ("oc_attn_plan_create", "oc_attn_plan_destroy", "oc_attn_workspace_size", "oc_attn_workspace_layout",
+           "oc_attn_prepare", "oc_attn_forward", "oc_attn_prepare_v_repair", "oc_attn_forward_v_repair",
+           "oc_attn_forward_prepared", "oc_attn_debug_pcodes", "oc_attn_status_string", "oc_attn_last_hip_error")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m bit_fp8_attention_block_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, VP, SZ, I32, I64, D = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+    st = ctypes.c_int
+    lib.oc_attn_plan_create.argtypes = [ctypes.POINTER(Desc), D, ctypes.POINTER(P)]
+    lib.oc_attn_plan_destroy.argtypes = [P]
+    lib.oc_attn_plan_destroy.restype = None
+    lib.oc_attn_workspace_size.argtypes = [P, ctypes.POINTER(SZ)]
+    lib.oc_attn_workspace_layout.argtypes = [P, ctypes.POINTER(WsLayout)]
+    lib.oc_attn_prepare.argtypes = [P, VP, VP, VP, VP, SZ, VP]
+    lib.oc_attn_forward.argtypes = [P, VP, VP, VP, VP, VP, SZ, VP]
+    lib.oc_attn_prepare_v_repair.argtypes = [P, VP, VP, VP, D, VP, SZ, VP]
+    lib.oc_attn_forward_v_repair.argtypes = [P, VP, VP, VP, D, VP, VP, SZ, VP]
+    lib.oc_attn_forward_prepared.argtypes = [P, VP, SZ, VP, ctypes.c_int, VP]
+    lib.oc_attn_debug_pcodes.argtypes = [P, VP, SZ, I32, I32, VP, VP, VP, VP]
+    lib.oc_attn_status_string.argtypes = [st]
+    lib.oc_attn_status_string.restype = ctypes.c_char_p
+    lib.oc_attn_last_hip_error.argtypes = []
+    for name in ("oc_attn_plan_create", "oc_attn_workspace_size", "oc_attn_workspace_layout", "oc_attn_prepare",
+                 "oc_attn_forward", "oc_attn_prepare_v_repair", "oc_attn_forward_v_repair",
+                 "oc_attn_forward_prepared", "oc_attn_debug_pcodes"):
+        getattr(lib, name).restype = st
+    del I64
+    return lib
+
+
+_lib = load_library()
+
+
+def _check(status, what):
+    if status != OC_OK:
+        msg = _lib.oc_attn_status_string(status).decode()
+        if status == OC_ERR_HIP:
+            msg += f" (hipError_t {_lib.oc_attn_last_hip_error()})"
+        raise OcAttnError(status, f"{what}: {msg}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+class Plan:
+    """One problem shape (and repair budget capacity) of the library."""
+
+    def __init__(self, B, S, H, dtype=torch.bfloat16, strides=None, softmax_scale=0.0, max_budget=0.0):
+        if strides is None:
+            strides = (S * H * 128, H * 128, 128)
+        dt = {torch.bfloat16: OC_BF16, torch.float16: OC_FP16}.get(dtype, 99)
+        self.desc = Desc(B, S, H, 128, dt, strides[0], strides[1], strides[2], float(softmax_scale or 0.0))
+        self.max_budget = float(max_budget)
+        self._p = ctypes.c_void_p()
+        _check(_lib.oc_attn_plan_create(ctypes.byref(self.desc), ctypes.c_double(self.max_budget),
+                                        ctypes.byref(self._p)), "oc_attn_plan_create")
+        n = ctypes.c_size_t()
+        _check(_lib.oc_attn_workspace_size(self._p, ctypes.byref(n)), "oc_attn_workspace_size")
+        self.workspace_bytes = n.value
+        self.layout = WsLayout()
+        _check(_lib.oc_attn_workspace_layout(self._p, ctypes.byref(self.layout)), "oc_attn_workspace_layout")
+
+    def __del__(self):
+        p = getattr(self, "_p", None)
+        if p is not None and p.value:
+            _lib.oc_attn_plan_destroy(p)
+            self._p = None
+
+    @property
+    def handle(self):
+        return self._p
+
+
+def _canon(q, k, v):
+    if q.dim() == 3:
+        q, k, v = q.unsqueeze(0), k.unsqueeze(0), v.unsqueeze(0)
+        squeeze = True
+    else:
+        squeeze = False
+    if q.dim() != 4 or q.shape[-1] != 128:
+        raise OcAttnError(OC_ERR_UNSUPPORTED, "inputs must be [B,S,H,128] or [S,H,128]")
+    if not (q.shape == k.shape == v.shape and q.stride() == k.stride() == v.stride()):
+        raise OcAttnError(OC_ERR_INVALID_ARGUMENT, "q, k, v must share shape and strides")
+    if not (q.dtype == k.dtype == v.dtype) or not q.is_cuda:
+        raise OcAttnError(OC_ERR_INVALID_ARGUMENT, "q, k, v must be GPU tensors of one dtype")
+    if q.stride(-1) != 1:
+        raise OcAttnError(OC_ERR_INVALID_ARGUMENT, "channel dimension must be contiguous")
+    return q, k, v, squeeze
+
+
+class Prepared:
+    """A workspace filled by prepare / prepare_v_repair, with its plan.
+    budget is None for a plain prepare."""
+
+    def __init__(self, plan, ws, shape, device, budget, softmax_scale):
+        self.plan, self.ws, self.shape, self.device = plan, ws, shape, device
+        self.budget, self.softmax_scale = budget, softmax_scale
+
+    def tensor(self, name, dtype, count):
+        off = getattr(self.plan.layout, name)
+        nbytes = count * torch.empty(0, dtype=dtype).element_size()
+        return self.ws[off:off + nbytes].view(dtype)
+
+
+_PLANS: dict = {}
+
+
+def get_plan(q, softmax_scale=None, max_budget=0.0):
+    B, S, H, _ = q.shape
+    key = (B, S, H, q.dtype, tuple(q.stride()[:3]), float(softmax_scale or 0.0), float(max_budget), q.device)
+    pl = _PLANS.get(key)
+    if pl is None:
+        pl = Plan(B, S, H, q.dtype, q.stride()[:3], softmax_scale or 0.0, max_budget)
+        if len(_PLANS) > 16:
+            _PLANS.clear()
+        _PLANS[key] = pl
+    return pl
+
+
+def _workspace(plan, device):
+    ws = getattr(plan, "_ws", None)
+    if ws is None or ws.device != device:
+        ws = torch.empty(plan.workspace_bytes + 256, dtype=torch.uint8, device=device)
+        pad = (-ws.data_ptr()) % 256
+        ws = ws[pad:pad + plan.workspace_bytes]
+        plan._ws = ws
+    return ws
+
+
+def prepare(q, k, v, budget=None, softmax_scale=None) -> Prepared:
+    """Quantize q, k, v into a workspace owned by the returned object. With a
+    budget (prepare_v_repair), also rank the value tokens by residual energy
+    and quantize the residuals of the top ceil(budget*S) of every (b, h)."""
+    q, k, v, _ = _canon(q, k, v)
+    plan = get_plan(q, softmax_scale, budget or 0.0)
+    ws = torch.empty(plan.workspace_bytes + 256, dtype=torch.uint8, device=q.device)
+    pad = (-ws.data_ptr()) % 256
+    ws = ws[pad:pad + plan.workspace_bytes]
+    st = _stream(q.device)
+    if budget is not None:
+        _check(_lib.oc_attn_prepare_v_repair(plan.handle, _ptr(q), _ptr(k), _ptr(v), ctypes.c_double(budget),
+                                             _ptr(ws), ws.numel(), st), "oc_attn_prepare_v_repair")
+    else:
+        _check(_lib.oc_attn_prepare(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(ws), ws.numel(), st),
+               "oc_attn_prepare")
+    return Prepared(plan, ws, tuple(q.shape), q.device, budget, softmax_scale)
+
+
+def prepare_v_repair(q, k, v, budget, softmax_scale=None) -> Prepared:
+    return prepare(q, k, v, budget, softmax_scale)
+
+
+def attention(q, k, v, softmax_scale=None, out=None):
+    """Full call: FP8 quantization + ExpCast attention, BF16 output."""
+    q, k, v, squeeze = _canon(q, k, v)
+    plan = get_plan(q, softmax_scale, 0.0)
+    ws = _workspace(plan, q.device)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    _check(_lib.oc_attn_forward(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ws), ws.numel(),
+                                _stream(q.device)), "oc_attn_forward")
+    return out.squeeze(0) if squeeze else out
+
+
+def attention_v_repair(q, k, v, budget, softmax_scale=None, out=None):
+    """Full call with V-residual repair of the ceil(budget*S) worst-rounded
+    value tokens of every (b, h)."""
+    q, k, v, squeeze = _canon(q, k, v)
+    plan = get_plan(q, softmax_scale, budget)
+    ws = _workspace(plan, q.device)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    _check(_lib.oc_attn_forward_v_repair(plan.handle, _ptr(q), _ptr(k), _ptr(v), ctypes.c_double(budget), _ptr(out),
+                                         _ptr(ws), ws.numel(), _stream(q.device)), "oc_attn_forward_v_repair")
+    return out.squeeze(0) if squeeze else out
+
+
+def attention_prepared(prep: Prepared, with_repair=None, out=None):
+    """Attention only, on a workspace filled by prepare / prepare_v_repair."""
+    if with_repair is None:
+        with_repair = prep.budget is not None
+    if out is None:
+        out = torch.empty(prep.shape, dtype=torch.bfloat16, device=prep.device)
+    _check(_lib.oc_attn_forward_prepared(prep.plan.handle, _ptr(prep.ws), prep.ws.numel(), _ptr(out),
+                                         int(bool(with_repair)), _stream(prep.device)), "oc_attn_forward_prepared")
+    return out
+
+
+def debug_pcodes(prep: Prepared, b: int, h: int):
+    """Bytes the attention kernel wrote for every (query, key) of one (b, h),
+    the running row max it used per key tile, and the output."""
+    B, S, H, _ = prep.shape
+    nT = prep.plan.layout.n_ktiles
+    codes = torch.zeros((S, S), dtype=torch.uint8, device=prep.device)
+    m_used = torch.full((S, nT), -(1 << 30), dtype=torch.int32, device=prep.device)
+    out = torch.zeros(prep.shape, dtype=torch.bfloat16, device=prep.device)
+    _check(_lib.oc_attn_debug_pcodes(prep.plan.handle, _ptr(prep.ws), prep.ws.numel(), b, h, _ptr(codes),
+                                     _ptr(m_used), _ptr(out), _stream(prep.device)), "oc_attn_debug_pcodes")
+    return codes, m_used, out
+
+
+def flops(B, S, H, D=128):
+    """Attention FLOPs counted as 4*B*S^2*H*D (QK^T and PV)."""
+    return 4.0 * B * S * S * H * D
+
+
+__all__ = ["attention", "attention_v_repair", "prepare", "prepare_v_repair", "attention_prepared", "debug_pcodes",
+           "Plan", "Prepared", "OcAttnError", "flops", "load_library", "EXPORTS", "LIB_PATH"]

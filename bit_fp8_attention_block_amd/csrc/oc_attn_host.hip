@@ -1,0 +1,422 @@
+// Host side of liboc_attn.so: the C ABI declared in include/oc_attn.h.
+// Validation happens before any HIP call, so every argument error is
+// reported the same way with or without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/oc_attn.h"
+#include "oc_common.h"
+#include "oc_kernels.h"
+
+using namespace oc;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+oc_status hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return OC_ERR_HIP;
+}
+
+inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+int repair_count(double budget, int S) {
+  // ceil(budget * S) with a 1e-9 allowance for binary rounding, capped at S
+  if (!(budget > 0.0)) return 0;
+  const double k = std::ceil(budget * (double)S - 1e-9);
+  if (k <= 0.0) return 0;
+  return k >= (double)S ? S : (int)k;
+}
+
+bool env_flag(const char* name) {
+  const char* s = std::getenv(name);
+  return s && *s && std::strcmp(s, "0") != 0;
+}
+
+}  // namespace
+
+struct oc_attn_plan {
+  oc_attn_desc d;
+  double max_budget;
+  float tau;
+  int n_sel_max;
+  oc_attn_ws_layout L;
+  int qbw;
+  int order;
+  // cached prepare graph
+  hipGraphExec_t gexec = nullptr;
+  hipStream_t cap_stream = nullptr;
+  const void *gq = nullptr, *gk = nullptr, *gv = nullptr;
+  void* gws = nullptr;
+  int gnsel = -1;
+  // the workspaces this plan prepared most recently, with their repair count
+  // (-1: prepared without repair)
+  static constexpr int NPREP = 8;
+  const void* prepared_ws[NPREP] = {};
+  int prepared_nsel[NPREP] = {};
+  int prepared_next = 0;
+
+  void mark_prepared(const void* ws, int nsel) {
+    for (int i = 0; i < NPREP; ++i)
+      if (prepared_ws[i] == ws) {
+        prepared_nsel[i] = nsel;
+        return;
+      }
+    prepared_ws[prepared_next] = ws;
+    prepared_nsel[prepared_next] = nsel;
+    prepared_next = (prepared_next + 1) % NPREP;
+  }
+  // repair count the workspace was prepared with; -2 if this plan never prepared it
+  int prepared_state(const void* ws) const {
+    for (int i = 0; i < NPREP; ++i)
+      if (prepared_ws[i] == ws) return prepared_nsel[i];
+    return -2;
+  }
+};
+
+static void compute_layout(oc_attn_plan* p) {
+  const oc_attn_desc& d = p->d;
+  const uint64_t BH = (uint64_t)d.B * d.H;
+  oc_attn_ws_layout& L = p->L;
+  std::memset(&L, 0, sizeof(L));
+  L.n_ktiles = (d.S + KTILE - 1) / KTILE;
+  L.n_qtiles = (d.S + BQ - 1) / BQ;
+  L.s_pad_q = L.n_qtiles * BQ;
+  L.n_sel_max = p->n_sel_max;
+  L.n_sel_tiles_max = (p->n_sel_max + KTILE - 1) / KTILE;
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) {
+    const uint64_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  L.qhat = take(BH * L.s_pad_q * HEAD_DIM);
+  L.kpack = take(BH * L.n_ktiles * (uint64_t)TILE_BYTES);
+  L.vpack = take(BH * L.n_ktiles * (uint64_t)TILE_BYTES);
+  L.sq = take(BH * (L.s_pad_q / KTILE) * 4);
+  L.sk = take(BH * L.n_ktiles * 4);
+  L.vamax = take(BH * L.n_ktiles * 4);
+  L.sv = take(BH * 2 * 4);
+  if (p->n_sel_max > 0) {
+    L.energy = take(BH * (uint64_t)d.S * 8);
+    L.sel = take(BH * (uint64_t)p->n_sel_max * 4);
+    L.kselpack = take(BH * L.n_sel_tiles_max * (uint64_t)TILE_BYTES);
+    L.rpack = take(BH * L.n_sel_tiles_max * (uint64_t)TILE_BYTES);
+    L.sksel = take(BH * L.n_sel_tiles_max * (uint64_t)KTILE * 4);
+    L.sr = take(BH * 2 * 4);
+  }
+  L.total_bytes = off;
+}
+
+static bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+static uint64_t input_extent_bytes(const oc_attn_desc& d) {
+  return 2ull * ((uint64_t)(d.B - 1) * d.stride_b + (uint64_t)(d.S - 1) * d.stride_s +
+                 (uint64_t)(d.H - 1) * d.stride_h + HEAD_DIM);
+}
+
+static bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+static oc_status check_inputs(const oc_attn_plan* p, const void* q, const void* k, const void* v, const void* ws,
+                              size_t ws_bytes) {
+  if (!q || !k || !v || !ws) return OC_ERR_INVALID_ARGUMENT;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || ((uintptr_t)ws & 255u)) return OC_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < p->L.total_bytes) return OC_ERR_WORKSPACE_TOO_SMALL;
+  const uint64_t ext = input_extent_bytes(p->d);
+  if (overlap(ws, ws_bytes, q, ext) || overlap(ws, ws_bytes, k, ext) || overlap(ws, ws_bytes, v, ext))
+    return OC_ERR_INVALID_ARGUMENT;
+  return OC_OK;
+}
+
+static oc_status check_out(const oc_attn_plan* p, const void* out, const void* const* others, int n_others,
+                           const void* ws, size_t ws_bytes) {
+  if (!out || misaligned(out)) return OC_ERR_INVALID_ARGUMENT;
+  const uint64_t on = 2ull * p->d.B * p->d.S * p->d.H * HEAD_DIM;
+  const uint64_t ext = input_extent_bytes(p->d);
+  for (int i = 0; i < n_others; ++i)
+    if (others[i] && overlap(out, on, others[i], ext)) return OC_ERR_INVALID_ARGUMENT;
+  if (overlap(out, on, ws, ws_bytes)) return OC_ERR_INVALID_ARGUMENT;
+  return OC_OK;
+}
+
+static oc_status check_budget(const oc_attn_plan* p, double budget) {
+  if (!(budget >= 0.0) || !(budget <= 1.0) || std::isnan(budget)) return OC_ERR_INVALID_ARGUMENT;
+  if (repair_count(budget, p->d.S) > p->n_sel_max) return OC_ERR_INVALID_ARGUMENT;
+  return OC_OK;
+}
+
+static PrepArgs prep_args(const oc_attn_plan* p, const void* q, const void* k, const void* v, void* ws, int n_sel) {
+  const oc_attn_desc& d = p->d;
+  const oc_attn_ws_layout& L = p->L;
+  uint8_t* base = (uint8_t*)ws;
+  PrepArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.sb = d.stride_b;
+  a.ss = d.stride_s;
+  a.sh = d.stride_h;
+  a.B = d.B;
+  a.S = d.S;
+  a.H = d.H;
+  a.nT = L.n_ktiles;
+  a.nQB = L.s_pad_q / KTILE;
+  a.s_pad_q = L.s_pad_q;
+  a.qhat = base + L.qhat;
+  a.kpack = base + L.kpack;
+  a.vpack = base + L.vpack;
+  a.sq = (float*)(base + L.sq);
+  a.sk = (float*)(base + L.sk);
+  a.vamax = (float*)(base + L.vamax);
+  a.sv = (float*)(base + L.sv);
+  if (n_sel > 0) {
+    a.energy = (double*)(base + L.energy);
+    a.sel = (int32_t*)(base + L.sel);
+    a.kselpack = base + L.kselpack;
+    a.rpack = base + L.rpack;
+    a.sksel = (float*)(base + L.sksel);
+    a.sr = (float*)(base + L.sr);
+    a.n_sel = n_sel;
+    a.n_sel_tiles = (n_sel + KTILE - 1) / KTILE;
+  }
+  return a;
+}
+
+static AttnArgs attn_args(const oc_attn_plan* p, const void* ws, void* out, int n_sel) {
+  const oc_attn_desc& d = p->d;
+  const oc_attn_ws_layout& L = p->L;
+  const uint8_t* base = (const uint8_t*)ws;
+  AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.qhat = base + L.qhat;
+  a.kpack = base + L.kpack;
+  a.vpack = base + L.vpack;
+  a.sq = (const float*)(base + L.sq);
+  a.sk = (const float*)(base + L.sk);
+  a.sv = (const float*)(base + L.sv);
+  if (n_sel > 0) {
+    a.kselpack = base + L.kselpack;
+    a.rpack = base + L.rpack;
+    a.sksel = (const float*)(base + L.sksel);
+    a.sr = (const float*)(base + L.sr);
+    a.n_sel = n_sel;
+    a.n_sel_tiles = (n_sel + KTILE - 1) / KTILE;
+  }
+  a.out = (uint16_t*)out;
+  a.B = d.B;
+  a.S = d.S;
+  a.H = d.H;
+  a.nT = L.n_ktiles;
+  a.nQT = L.n_qtiles;
+  a.nQB = L.s_pad_q / KTILE;
+  a.s_pad_q = L.s_pad_q;
+  a.c8 = (float)(8.0 * (double)p->tau * 1.4426950408889634);
+  a.order = p->order;
+  return a;
+}
+
+// Enqueue the prepare kernels, through the plan's cached graph unless
+// OC_ATTN_NO_GRAPH is set. n_sel < 0: plain prepare; n_sel >= 0: prepare for
+// repair with that many selected tokens (0 selects none).
+static oc_status run_prepare(oc_attn_plan* p, const void* q, const void* k, const void* v, void* ws, int n_sel,
+                             hipStream_t st) {
+  const PrepArgs a = prep_args(p, q, k, v, ws, n_sel);
+  const bool fp16 = p->d.dtype == OC_FP16;
+  hipError_t e;
+  if (env_flag("OC_ATTN_NO_GRAPH")) {
+    e = launch_prepare(a, fp16, st);
+    if (e != hipSuccess) return hip_fail(e);
+  } else {
+    if (!(p->gexec && p->gq == q && p->gk == k && p->gv == v && p->gws == ws && p->gnsel == n_sel)) {
+      if (p->gexec) {
+        (void)hipGraphExecDestroy(p->gexec);
+        p->gexec = nullptr;
+      }
+      if (!p->cap_stream) {
+        e = hipStreamCreateWithFlags(&p->cap_stream, hipStreamNonBlocking);
+        if (e != hipSuccess) return hip_fail(e);
+      }
+      e = hipStreamBeginCapture(p->cap_stream, hipStreamCaptureModeThreadLocal);
+      if (e != hipSuccess) return hip_fail(e);
+      const hipError_t le = launch_prepare(a, fp16, p->cap_stream);
+      hipGraph_t graph = nullptr;
+      e = hipStreamEndCapture(p->cap_stream, &graph);
+      if (le != hipSuccess) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return hip_fail(le);
+      }
+      if (e != hipSuccess) return hip_fail(e);
+      e = hipGraphInstantiate(&p->gexec, graph, nullptr, nullptr, 0);
+      (void)hipGraphDestroy(graph);
+      if (e != hipSuccess) {
+        p->gexec = nullptr;
+        return hip_fail(e);
+      }
+      p->gq = q;
+      p->gk = k;
+      p->gv = v;
+      p->gws = ws;
+      p->gnsel = n_sel;
+    }
+    e = hipGraphLaunch(p->gexec, st);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  p->mark_prepared(ws, n_sel);
+  return OC_OK;
+}
+
+static oc_status run_attention(oc_attn_plan* p, const void* ws, void* out, int n_sel, hipStream_t st) {
+  const AttnArgs a = attn_args(p, ws, out, n_sel);
+  const hipError_t e = launch_attention(a, n_sel > 0, false, p->qbw, st);
+  return e == hipSuccess ? OC_OK : hip_fail(e);
+}
+
+extern "C" {
+
+oc_status oc_attn_plan_create(const oc_attn_desc* desc, double max_repair_budget, oc_attn_plan** plan) {
+  if (!desc || !plan) return OC_ERR_INVALID_ARGUMENT;
+  *plan = nullptr;
+  const oc_attn_desc& d = *desc;
+  if (d.D != HEAD_DIM) return OC_ERR_UNSUPPORTED;
+  if (d.dtype != OC_BF16 && d.dtype != OC_FP16) return OC_ERR_UNSUPPORTED;
+  if (d.B < 1 || d.S < 1 || d.H < 1) return OC_ERR_INVALID_ARGUMENT;
+  if (d.stride_b < 0 || d.stride_s < 0 || d.stride_h < 0) return OC_ERR_INVALID_ARGUMENT;
+  // 16-byte rows: every stride a multiple of 8 elements
+  if ((d.stride_b | d.stride_s | d.stride_h) & 7) return OC_ERR_INVALID_ARGUMENT;
+  if (!(d.softmax_scale >= 0.0f) || std::isinf(d.softmax_scale)) return OC_ERR_INVALID_ARGUMENT;
+  if (!(max_repair_budget >= 0.0 && max_repair_budget <= 1.0)) return OC_ERR_INVALID_ARGUMENT;
+  // index arithmetic in the kernels uses 32-bit tile and row counts
+  if ((int64_t)d.B * d.H * (((int64_t)d.S + BQ - 1) / BQ) > (int64_t)INT32_MAX / 8) return OC_ERR_UNSUPPORTED;
+  oc_attn_plan* p = new (std::nothrow) oc_attn_plan();
+  if (!p) return OC_ERR_INVALID_ARGUMENT;
+  p->d = d;
+  p->max_budget = max_repair_budget;
+  p->tau = d.softmax_scale > 0.0f ? d.softmax_scale : (float)(1.0 / std::sqrt((double)d.D));
+  p->n_sel_max = repair_count(max_repair_budget, d.S);
+  const char* qbw = std::getenv("OC_ATTN_QBW");
+  p->qbw = (qbw && std::atoi(qbw) == 2) ? 2 : 4;
+  const char* order = std::getenv("OC_ATTN_ORDER");
+  p->order = (order && std::atoi(order) == 1) ? 1 : 0;
+  compute_layout(p);
+  *plan = p;
+  return OC_OK;
+}
+
+void oc_attn_plan_destroy(oc_attn_plan* p) {
+  if (!p) return;
+  if (p->gexec) (void)hipGraphExecDestroy(p->gexec);
+  if (p->cap_stream) (void)hipStreamDestroy(p->cap_stream);
+  delete p;
+}
+
+oc_status oc_attn_workspace_size(const oc_attn_plan* p, size_t* bytes) {
+  if (!p || !bytes) return OC_ERR_INVALID_ARGUMENT;
+  *bytes = (size_t)p->L.total_bytes;
+  return OC_OK;
+}
+
+oc_status oc_attn_workspace_layout(const oc_attn_plan* p, oc_attn_ws_layout* layout) {
+  if (!p || !layout) return OC_ERR_INVALID_ARGUMENT;
+  *layout = p->L;
+  return OC_OK;
+}
+
+oc_status oc_attn_prepare(oc_attn_plan* p, const void* q, const void* k, const void* v, void* ws, size_t ws_bytes,
+                          void* stream) {
+  if (!p) return OC_ERR_INVALID_ARGUMENT;
+  oc_status s = check_inputs(p, q, k, v, ws, ws_bytes);
+  if (s != OC_OK) return s;
+  return run_prepare(p, q, k, v, ws, -1, (hipStream_t)stream);
+}
+
+oc_status oc_attn_forward(oc_attn_plan* p, const void* q, const void* k, const void* v, void* out, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (!p) return OC_ERR_INVALID_ARGUMENT;
+  oc_status s = check_inputs(p, q, k, v, ws, ws_bytes);
+  if (s != OC_OK) return s;
+  const void* ins[3] = {q, k, v};
+  s = check_out(p, out, ins, 3, ws, ws_bytes);
+  if (s != OC_OK) return s;
+  s = run_prepare(p, q, k, v, ws, -1, (hipStream_t)stream);
+  if (s != OC_OK) return s;
+  return run_attention(p, ws, out, 0, (hipStream_t)stream);
+}
+
+oc_status oc_attn_prepare_v_repair(oc_attn_plan* p, const void* q, const void* k, const void* v, double budget,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  if (!p) return OC_ERR_INVALID_ARGUMENT;
+  oc_status s = check_budget(p, budget);
+  if (s != OC_OK) return s;
+  s = check_inputs(p, q, k, v, ws, ws_bytes);
+  if (s != OC_OK) return s;
+  return run_prepare(p, q, k, v, ws, repair_count(budget, p->d.S), (hipStream_t)stream);
+}
+
+oc_status oc_attn_forward_v_repair(oc_attn_plan* p, const void* q, const void* k, const void* v, double budget,
+                                   void* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!p) return OC_ERR_INVALID_ARGUMENT;
+  oc_status s = check_budget(p, budget);
+  if (s != OC_OK) return s;
+  s = check_inputs(p, q, k, v, ws, ws_bytes);
+  if (s != OC_OK) return s;
+  const void* ins[3] = {q, k, v};
+  s = check_out(p, out, ins, 3, ws, ws_bytes);
+  if (s != OC_OK) return s;
+  const int n_sel = repair_count(budget, p->d.S);
+  s = run_prepare(p, q, k, v, ws, n_sel, (hipStream_t)stream);
+  if (s != OC_OK) return s;
+  return run_attention(p, ws, out, n_sel, (hipStream_t)stream);
+}
+
+oc_status oc_attn_forward_prepared(oc_attn_plan* p, const void* ws, size_t ws_bytes, void* out, int with_repair,
+                                   void* stream) {
+  if (!p || !ws || ((uintptr_t)ws & 255u)) return OC_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < p->L.total_bytes) return OC_ERR_WORKSPACE_TOO_SMALL;
+  oc_status s = check_out(p, out, nullptr, 0, ws, ws_bytes);
+  if (s != OC_OK) return s;
+  const int state = p->prepared_state(ws);
+  if (state == -2) return OC_ERR_NOT_PREPARED;
+  if (with_repair && state < 0) return OC_ERR_NOT_PREPARED;
+  return run_attention(p, ws, out, with_repair ? state : 0, (hipStream_t)stream);
+}
+
+oc_status oc_attn_debug_pcodes(oc_attn_plan* p, const void* ws, size_t ws_bytes, int32_t b, int32_t h,
+                               uint8_t* codes, int32_t* m_used, void* out, void* stream) {
+  if (!p || !ws || !codes || !m_used || !out) return OC_ERR_INVALID_ARGUMENT;
+  if (b < 0 || b >= p->d.B || h < 0 || h >= p->d.H) return OC_ERR_INVALID_ARGUMENT;
+  if (p->d.S > 8192) return OC_ERR_UNSUPPORTED;
+  if (ws_bytes < p->L.total_bytes) return OC_ERR_WORKSPACE_TOO_SMALL;
+  if (p->prepared_state(ws) == -2) return OC_ERR_NOT_PREPARED;
+  AttnArgs a = attn_args(p, ws, out, 0);
+  a.dump_codes = codes;
+  a.dump_m = m_used;
+  a.dump_b = b;
+  a.dump_h = h;
+  const hipError_t e = launch_attention(a, false, true, p->qbw, (hipStream_t)stream);
+  return e == hipSuccess ? OC_OK : hip_fail(e);
+}
+
+const char* oc_attn_status_string(oc_status s) {
+  switch (s) {
+    case OC_OK: return "ok";
+    case OC_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case OC_ERR_UNSUPPORTED: return "unsupported (D must be 128; dtype bf16 or fp16)";
+    case OC_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case OC_ERR_NOT_PREPARED: return "workspace not prepared by this plan";
+    case OC_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+int oc_attn_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// Kernel argument blocks and launchers shared by the host library and the
+// kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace oc {
+
+struct PrepArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t sb, ss, sh;          // element strides shared by q, k, v
+  int B, S, H;
+  int nT, nQB, s_pad_q;        // key tiles, Q scale blocks, padded Q rows
+  uint8_t* qhat;
+  uint8_t* kpack;
+  uint8_t* vpack;
+  float* sq;
+  float* sk;
+  float* vamax;
+  float* sv;                   // [B][H][2]: amax/448, 448/amax
+  // repair (energy == nullptr: no repair)
+  double* energy;
+  int32_t* sel;
+  uint8_t* kselpack;
+  uint8_t* rpack;
+  float* sksel;
+  float* sr;                   // [B][H][2]
+  int n_sel, n_sel_tiles;
+};
+
+struct AttnArgs {
+  const uint8_t* qhat;
+  const uint8_t* kpack;
+  const uint8_t* vpack;
+  const float* sq;
+  const float* sk;
+  const float* sv;
+  const uint8_t* kselpack;
+  const uint8_t* rpack;
+  const float* sksel;
+  const float* sr;
+  int n_sel, n_sel_tiles;
+  uint16_t* out;               // bf16 [B][S][H][128], contiguous
+  int B, S, H, nT, nQT, nQB, s_pad_q;
+  float c8;                    // 8 * tau * log2(e)
+  int order;                   // 0: mid-window (from the query tile outward), 1: ascending
+  uint8_t* dump_codes;         // debug: [S][S] bytes for one (b, h)
+  int32_t* dump_m;             // debug: [S][nT]
+  int dump_b, dump_h;
+};
+
+hipError_t launch_prepare(const PrepArgs& a, bool fp16, hipStream_t st);
+hipError_t launch_attention(const AttnArgs& a, bool repair, bool dump, int qbw, hipStream_t st);
+
+}  // namespace oc

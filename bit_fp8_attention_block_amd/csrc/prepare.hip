@@ -1,0 +1,421 @@
+// Prepare kernels: BF16/FP16 Q, K, V -> E4M3 codes and scales in the
+// workspace, plus the V-residual repair set.
+//
+// Follows the Open VC Attention product page (kernel paragraph: per-block Q/K
+// scales, per-head V scale, V packed transposed for the matrix cores) and the
+// Open-VC news page ("Архитектурные оптимизации": input preparation fused
+// into one graph; "Решение: ExpCast ...": residual repair of the worst-rounded
+// value tokens). All four kernels are memory-bound; see oc_attn.h for the
+// workspace layouts they write.
+#include "oc_common.h"
+#include "oc_kernels.h"
+
+namespace oc {
+
+// Load 16 consecutive 16-bit channels [16*oc, 16*oc+16) of one token, or
+// zeros for a token beyond S.
+__device__ inline void load16(const uint16_t* base, bool valid, uint4& lo, uint4& hi) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  if (valid) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(base);
+    const u32x4 x = __builtin_nontemporal_load(p), y = __builtin_nontemporal_load(p + 1);
+    lo = make_uint4(x[0], x[1], x[2], x[3]);
+    hi = make_uint4(y[0], y[1], y[2], y[3]);
+  } else {
+    lo = make_uint4(0, 0, 0, 0);
+    hi = lo;
+  }
+}
+
+// max |x| bit pattern over 16 packed halves (sign dropped; bf16 and fp16
+// magnitudes order like their bit patterns)
+__device__ inline uint32_t absmax_bits(uint4 lo, uint4 hi, uint32_t m) {
+  uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t x = w[i] & 0x7FFF7FFFu;
+    m = max(m, max(x & 0xFFFFu, x >> 16));
+  }
+  return m;
+}
+
+template <bool FP16>
+__device__ inline float bits_to_f32(uint32_t h) { return half_to_f32<FP16>(h); }
+
+// 16 halves -> 16 E4M3 bytes of x * inv
+template <bool FP16>
+__device__ inline uint4 encode16(uint4 lo, uint4 hi, float inv) {
+  uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t a = w[2 * i], b = w[2 * i + 1];
+    uint32_t p0 = e4m3_encode2(bits_to_f32<FP16>(a & 0xFFFFu) * inv, bits_to_f32<FP16>(a >> 16) * inv);
+    uint32_t p1 = e4m3_encode2(bits_to_f32<FP16>(b & 0xFFFFu) * inv, bits_to_f32<FP16>(b >> 16) * inv);
+    o[i] = p0 | (p1 << 16);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// block-wide max of a non-negative value (blockDim.x threads, <= 1024)
+__device__ inline float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float m = 0.0f;
+  for (int i = 0; i < nw; ++i) m = __builtin_fmaxf(m, red[i]);
+  return m;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 1: per (b, h, 128-token block): Q and K block amax, scales, codes;
+// V block amax (the per-head V scale needs all blocks first).
+// grid (nQB, H, B), 256 threads; thread -> rows {32p + tid/8}, channels 16*(tid%8)..+16
+template <bool FP16>
+__global__ __launch_bounds__(256) void prep_qk_kernel(PrepArgs a) {
+  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, rsub = tid >> 3, oc = tid & 7;
+  const int bh = b * a.H + h;
+  const bool kv = blk < a.nT;
+  __shared__ float red[16];
+
+  uint4 ql[4], qh[4], kl[4], kh[4];
+  uint32_t mq = 0, mk = 0, mv = 0;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int tok = blk * KTILE + 32 * p + rsub;
+    const bool valid = tok < a.S;
+    const int64_t off = (int64_t)b * a.sb + (int64_t)tok * a.ss + (int64_t)h * a.sh + 16 * oc;
+    load16(a.q + off, valid, ql[p], qh[p]);
+    mq = absmax_bits(ql[p], qh[p], mq);
+    load16(a.k + off, valid && kv, kl[p], kh[p]);
+    mk = absmax_bits(kl[p], kh[p], mk);
+    uint4 vl, vh;
+    load16(a.v + off, valid && kv, vl, vh);
+    mv = absmax_bits(vl, vh, mv);
+  }
+  const float amq = block_max(bits_to_f32<FP16>(mq), red);
+  const float amk = block_max(bits_to_f32<FP16>(mk), red + 4);
+  const float amv = block_max(bits_to_f32<FP16>(mv), red + 8);
+  float sq, iq, sk, ik;
+  quant_scales(amq, sq, iq);
+  quant_scales(amk, sk, ik);
+  if (tid == 0) {
+    a.sq[(int64_t)bh * a.nQB + blk] = sq;
+    if (kv) {
+      a.sk[(int64_t)bh * a.nT + blk] = sk;
+      a.vamax[(int64_t)bh * a.nT + blk] = amv;
+    }
+  }
+  uint8_t* qdst = a.qhat + ((int64_t)bh * a.s_pad_q + (int64_t)blk * KTILE) * HEAD_DIM;
+  uint8_t* kdst = a.kpack + ((int64_t)bh * a.nT + blk) * TILE_BYTES;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int row = 32 * p + rsub;
+    *reinterpret_cast<uint4*>(qdst + row * HEAD_DIM + 16 * oc) = encode16<FP16>(ql[p], qh[p], iq);
+    if (kv) *reinterpret_cast<uint4*>(kdst + swz(row, 16 * oc)) = encode16<FP16>(kl[p], kh[p], ik);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 2: per (b, h, key tile): head V scale from the block maxima, V codes
+// transposed and packed into the PV operand order (through LDS), and with
+// repair the residual energy of every token.
+// grid (nT, H, B), 256 threads; thread -> tokens 4m..4m+3 (m = tid/8), channels 16*(tid%8)..+16
+template <bool FP16, bool REPAIR>
+__global__ __launch_bounds__(256) void prep_v_kernel(PrepArgs a) {
+  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, m = tid >> 3, oc = tid & 7;
+  const int bh = b * a.H + h;
+  __shared__ float red[16];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[TILE_BYTES];
+
+  float mx = 0.0f;
+  for (int i = tid; i < a.nT; i += 256) mx = __builtin_fmaxf(mx, a.vamax[(int64_t)bh * a.nT + i]);
+  const float amax = block_max(mx, red);
+  float sv, inv;
+  quant_scales(amax, sv, inv);
+  if (tile == 0 && tid == 0) {
+    a.sv[2 * bh] = sv;
+    a.sv[2 * bh + 1] = inv;
+  }
+
+  uint4 lo[4], hi[4], cd[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int tok = tile * KTILE + 4 * m + r;
+    const int64_t off = (int64_t)b * a.sb + (int64_t)tok * a.ss + (int64_t)h * a.sh + 16 * oc;
+    load16(a.v + off, tok < a.S, lo[r], hi[r]);
+    cd[r] = encode16<FP16>(lo[r], hi[r], inv);
+  }
+  // transpose: channel d = 16*oc + c gets the 4 bytes of tokens 4m..4m+3,
+  // which sit in 4 consecutive columns of the packed tile
+  const int kcol = vcol_of_key(4 * m);
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const uint32_t sh = 8 * (c & 3);
+    const int wsel = c >> 2;
+    uint32_t w = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t word = (wsel == 0) ? cd[r].x : (wsel == 1) ? cd[r].y : (wsel == 2) ? cd[r].z : cd[r].w;
+      w |= ((word >> sh) & 0xFFu) << (8 * r);
+    }
+    *reinterpret_cast<uint32_t*>(lds + swz(16 * oc + c, kcol)) = w;
+  }
+  __syncthreads();
+  uint8_t* dst = a.vpack + ((int64_t)bh * a.nT + tile) * TILE_BYTES;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int o = (i * 256 + tid) * 16;
+    *reinterpret_cast<uint4*>(dst + o) = *reinterpret_cast<const uint4*>(lds + o);
+  }
+
+  if (REPAIR) {
+    // residual r = v - sv*dec(code) in fp32 (two roundings, no fusion);
+    // energy = sum of r^2 over the 128 channels in float64
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t w[8] = {lo[r].x, lo[r].y, lo[r].z, lo[r].w, hi[r].x, hi[r].y, hi[r].z, hi[r].w};
+      const uint32_t cw[4] = {cd[r].x, cd[r].y, cd[r].z, cd[r].w};
+      double e = 0.0;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const float x = bits_to_f32<FP16>((w[c >> 1] >> (16 * (c & 1))) & 0xFFFFu);
+        const float t = __fmul_rn(sv, e4m3_decode((cw[c >> 2] >> (8 * (c & 3))) & 0xFFu));
+        const double d = (double)__fsub_rn(x, t);
+        e = __builtin_fma(d, d, e);
+      }
+      e += __shfl_xor(e, 1, 64);
+      e += __shfl_xor(e, 2, 64);
+      e += __shfl_xor(e, 4, 64);
+      const int tok = tile * KTILE + 4 * m + r;
+      if (oc == 0 && tok < a.S) a.energy[(int64_t)bh * a.S + tok] = e;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// block-wide exclusive prefix sum (1024 threads)
+__device__ inline int block_exclusive_scan(int v, int* scratch, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) scratch[w] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+  const int nw = blockDim.x >> 6;
+  for (int i = 0; i < nw; ++i) {
+    if (i < w) before += scratch[i];
+    tot += scratch[i];
+  }
+  total = tot;
+  return before + x - v;
+}
+
+// residual of one value element, recomputed exactly as prep_v_kernel does
+template <bool FP16>
+__device__ inline float residual(uint32_t hbits, float sv, float inv) {
+  const float x = bits_to_f32<FP16>(hbits);
+  const uint32_t code = e4m3_encode2(x * inv, 0.0f) & 0xFFu;
+  return __fsub_rn(x, __fmul_rn(sv, e4m3_decode(code)));
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 3: per (b, h): top-k tokens by residual energy (radix select on the
+// float64 bit patterns, which order like the non-negative values), ties to
+// the lower index, written in ascending token order; then the amax of the
+// selected residuals gives the residual scale.
+// grid (H, B), 1024 threads
+template <bool FP16>
+__global__ __launch_bounds__(1024) void select_kernel(PrepArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int bh = b * a.H + h;
+  const int S = a.S, k = a.n_sel;
+  const uint64_t* e = reinterpret_cast<const uint64_t*>(a.energy + (int64_t)bh * S);
+  __shared__ uint32_t hist[256];
+  __shared__ int scratch[16];
+  __shared__ uint64_t s_prefix;
+  __shared__ int s_krem;
+  __shared__ float red[16];
+
+  uint64_t prefix = 0, mask = 0;
+  int krem = k;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < S; i += 1024) {
+      const uint64_t u = e[i];
+      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int cum = 0, bin = 255;
+      for (; bin > 0; --bin) {
+        if (cum + (int)hist[bin] >= krem) break;
+        cum += (int)hist[bin];
+      }
+      s_prefix = prefix | ((uint64_t)bin << shift);
+      s_krem = krem - cum;
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    krem = s_krem;
+    mask |= (uint64_t)255 << shift;
+  }
+  // prefix = bits of the k-th largest energy T; krem = how many tokens equal to T to take
+  const int chunk = (S + 1023) / 1024;
+  const int i0 = min(S, tid * chunk), i1 = min(S, i0 + chunk);
+  int gt = 0, eq = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint64_t u = e[i];
+    gt += u > prefix;
+    eq += u == prefix;
+  }
+  int tot;
+  const int eq_before = block_exclusive_scan(eq, scratch, tot);
+  const int take_eq = max(0, min(eq, krem - eq_before));
+  int pos = block_exclusive_scan(gt + take_eq, scratch, tot);
+  int32_t* sel = a.sel + (int64_t)bh * a.n_sel;
+  int taken = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint64_t u = e[i];
+    if (u > prefix || (u == prefix && taken < take_eq)) {
+      sel[pos++] = i;
+      if (u == prefix) ++taken;
+    }
+  }
+  __threadfence_block();
+  __syncthreads();
+
+  // residual amax over the selected tokens (8-channel chunks)
+  const float sv = a.sv[2 * bh], inv = a.sv[2 * bh + 1];
+  float mx = 0.0f;
+  for (int it = tid; it < k * 16; it += 1024) {
+    const int slot = it >> 4, c8 = (it & 15) * 8;
+    const int tok = sel[slot];
+    const int64_t off = (int64_t)b * a.sb + (int64_t)tok * a.ss + (int64_t)h * a.sh + c8;
+    const uint4 w = *reinterpret_cast<const uint4*>(a.v + off);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float r = residual<FP16>((ws[c >> 1] >> (16 * (c & 1))) & 0xFFFFu, sv, inv);
+      mx = __builtin_fmaxf(mx, __builtin_fabsf(r));
+    }
+  }
+  const float amax = block_max(mx, red);
+  if (tid == 0) {
+    float s, i;
+    quant_scales(amax, s, i);
+    a.sr[2 * bh] = s;
+    a.sr[2 * bh + 1] = i;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 4: per (b, h, slot tile): gather the selected K rows (codes and
+// block scales) and pack the E4M3 residuals like V.
+// grid (nTs, H, B), 256 threads
+template <bool FP16>
+__global__ __launch_bounds__(256) void pack_repair_kernel(PrepArgs a) {
+  const int ts = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int bh = b * a.H + h;
+  const int k = a.n_sel;
+  const int nslot = a.n_sel_tiles * KTILE;
+  const int32_t* sel = a.sel + (int64_t)bh * a.n_sel;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[TILE_BYTES];
+
+  // K rows: thread -> slot tid/2, chunks 4*(tid%2)..+4
+  {
+    const int sl = tid >> 1, half = tid & 1;
+    const int slot = ts * KTILE + sl;
+    uint8_t* dst = a.kselpack + ((int64_t)bh * a.n_sel_tiles + ts) * TILE_BYTES;
+    if (slot < k) {
+      const int j = sel[slot];
+      const uint8_t* src = a.kpack + ((int64_t)bh * a.nT + (j >> 7)) * TILE_BYTES;
+      const int sr = j & 127;
+#pragma unroll
+      for (int c = 4 * half; c < 4 * half + 4; ++c)
+        *reinterpret_cast<uint4*>(dst + swz(sl, 16 * c)) = *reinterpret_cast<const uint4*>(src + swz(sr, 16 * c));
+      if (half == 0) a.sksel[(int64_t)bh * nslot + slot] = a.sk[(int64_t)bh * a.nT + (j >> 7)];
+    } else {
+#pragma unroll
+      for (int c = 4 * half; c < 4 * half + 4; ++c)
+        *reinterpret_cast<uint4*>(dst + swz(sl, 16 * c)) = make_uint4(0, 0, 0, 0);
+      if (half == 0) a.sksel[(int64_t)bh * nslot + slot] = 0.0f;
+    }
+  }
+  // residual codes, transposed like V: thread -> slots 4m..4m+3, channels 16*oc..+16
+  const int m = tid >> 3, oc = tid & 7;
+  const float sv = a.sv[2 * bh], inv = a.sv[2 * bh + 1];
+  const float rinv = a.sr[2 * bh + 1];
+  uint32_t cw[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int slot = ts * KTILE + 4 * m + r;
+    uint4 lo, hi;
+    const int tok = slot < k ? sel[slot] : 0;
+    const int64_t off = (int64_t)b * a.sb + (int64_t)tok * a.ss + (int64_t)h * a.sh + 16 * oc;
+    load16(a.v + off, slot < k, lo, hi);
+    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float r0 = residual<FP16>(w[2 * q] & 0xFFFFu, sv, inv) * rinv;
+      const float r1 = residual<FP16>(w[2 * q] >> 16, sv, inv) * rinv;
+      const float r2 = residual<FP16>(w[2 * q + 1] & 0xFFFFu, sv, inv) * rinv;
+      const float r3 = residual<FP16>(w[2 * q + 1] >> 16, sv, inv) * rinv;
+      cw[r][q] = e4m3_encode2(r0, r1) | (e4m3_encode2(r2, r3) << 16);
+    }
+  }
+  const int kcol = vcol_of_key(4 * m);
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) w |= ((cw[r][c >> 2] >> (8 * (c & 3))) & 0xFFu) << (8 * r);
+    *reinterpret_cast<uint32_t*>(lds + swz(16 * oc + c, kcol)) = w;
+  }
+  __syncthreads();
+  uint8_t* dst = a.rpack + ((int64_t)bh * a.n_sel_tiles + ts) * TILE_BYTES;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int o = (i * 256 + tid) * 16;
+    *reinterpret_cast<uint4*>(dst + o) = *reinterpret_cast<const uint4*>(lds + o);
+  }
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_prepare(const PrepArgs& a, bool fp16, hipStream_t st) {
+  const dim3 g1(a.nQB, a.H, a.B), g2(a.nT, a.H, a.B);
+  const bool rep = a.energy != nullptr;
+  if (fp16) {
+    hipLaunchKernelGGL(prep_qk_kernel<true>, g1, dim3(256), 0, st, a);
+    if (rep) hipLaunchKernelGGL((prep_v_kernel<true, true>), g2, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((prep_v_kernel<true, false>), g2, dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(prep_qk_kernel<false>, g1, dim3(256), 0, st, a);
+    if (rep) hipLaunchKernelGGL((prep_v_kernel<false, true>), g2, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((prep_v_kernel<false, false>), g2, dim3(256), 0, st, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !rep || a.n_sel == 0) return e;
+  const dim3 g3(a.H, a.B), g4(a.n_sel_tiles, a.H, a.B);
+  if (fp16) {
+    hipLaunchKernelGGL(select_kernel<true>, g3, dim3(1024), 0, st, a);
+    hipLaunchKernelGGL(pack_repair_kernel<true>, g4, dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(select_kernel<false>, g3, dim3(1024), 0, st, a);
+    hipLaunchKernelGGL(pack_repair_kernel<false>, g4, dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace oc

@@ -1,0 +1,185 @@
+/*
+ * oc_attn — ExpCast FP8 forward attention on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of liboc_attn.so. Plain pointers and sizes only.
+ *
+ * What the library computes (sources are the pages on Open-VC Attention and
+ * VC-Attention):
+ *   - Open VC Attention product page (ailibri.com), API paragraph:
+ *     non-causal multi-head forward attention with head dimension 128 on
+ *     FP16 or BF16 inputs laid out [B,S,H,128] (or [S,H,128]). The call
+ *     quantizes to FP8 itself, runs ExpCast attention, and returns BF16.
+ *   - same page, kernel paragraph: softmax weights go to FP8 straight from
+ *     the scores. Q and K carry per-block scales and V a per-head scale.
+ *     Key tiles are visited starting from the middle of the window.
+ *   - VC-Attention write-up (Nunchux AI), section "ExpCast-FP8": the FP8 byte
+ *     of a weight is produced from the log-domain score with one fused
+ *     multiply-add (E4M3 byte as integer ~ 8*log2(v) + 56, beta = -0.35),
+ *     with no exponential and no FP32->FP8 conversion.
+ *   - Open-VC news (aikraft.ru), sections "Решение: ExpCast и отказ от
+ *     экспонент" (V-residual repair of the worst-rounded value tokens) and
+ *     "Архитектурные оптимизации" (mid-window traversal; Q/K/V preparation
+ *     fused into one graph); product page, repair paragraph (prepare with a
+ *     budget such as 0.005, then the repaired attention call).
+ *
+ * Per (b, h), with tau the softmax scale:
+ *   Q/K: per 128-token block, s = amax/448 (fp32). The code is E4M3(q * 448/amax),
+ *        round to nearest even, saturating.
+ *   V:   one scale per head, sv = amax/448, same rounding.
+ *   x_ij  = tau*log2(e) * sq_i * sk_j * <q_hat_i, k_hat_j>
+ *   M_i   = ceil(max_j x_ij)                      (bit-aligned row max)
+ *   c_ij  = clamp(rne(8*(x_ij - M_i) + 119.65), 0, 126)   (E4M3 byte of 256*2^(x-M))
+ *   L_i   = sum_j dec(c_ij)
+ *   O_i   = sv * sum_j dec(c_ij) v_hat_j / L_i    -> BF16
+ *   repair (budget b): the k = ceil(b*S) tokens with the largest residual
+ *   energy sum_c (v - sv*dec(v_hat))^2 get sr * dec(r_hat_j) added to their
+ *   value. r_hat is the E4M3 residual with its own per-head scale sr. L is
+ *   left unchanged.
+ *
+ * Layout: q, k and v are [B,S,H,128] with element strides (stride_b,
+ * stride_s, stride_h) shared by the three tensors; the channel stride is 1.
+ * `out` is a contiguous BF16 [B,S,H,128] tensor. q, k, v and out must be
+ * 16-byte aligned and every stride a multiple of 8 elements; the workspace
+ * must be 256-byte aligned.
+ *
+ * Ownership: the caller allocates and owns q, k, v, out and the workspace
+ * (device memory). The library never allocates or frees device memory in
+ * these calls. A plan owns only host state: the descriptor, its sizes, and a
+ * cached hipGraphExec of the prepare step, keyed on the pointers it was
+ * captured with. A plan is used from one host thread at a time.
+ *
+ * Execution: every call enqueues work on `stream` (a hipStream_t; NULL is the
+ * default stream) and returns without synchronizing. Inputs are never
+ * modified. `out` must not overlap q, k, v or the workspace.
+ *
+ * Errors: every call returns an oc_status. Arguments are validated before
+ * anything is enqueued:
+ *   - D != 128 or an unknown dtype gives OC_ERR_UNSUPPORTED;
+ *   - B, S or H < 1, a NULL or misaligned pointer, a negative stride, a
+ *     budget outside [0, max budget of the plan] or NaN, or overlapping
+ *     buffers give OC_ERR_INVALID_ARGUMENT;
+ *   - a workspace smaller than oc_attn_workspace_size gives
+ *     OC_ERR_WORKSPACE_TOO_SMALL;
+ *   - oc_attn_forward_prepared on a workspace this plan has not prepared
+ *     (or, with repair, not prepared with repair) gives OC_ERR_NOT_PREPARED.
+ *   A failing HIP call gives OC_ERR_HIP. oc_attn_last_hip_error() then
+ *   returns the hipError_t of the calling thread's last failure.
+ * NaN or Inf inputs are not supported; the output for them is undefined.
+ */
+#ifndef OC_ATTN_H
+#define OC_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum oc_status {
+  OC_OK = 0,
+  OC_ERR_INVALID_ARGUMENT = 1,
+  OC_ERR_UNSUPPORTED = 2,
+  OC_ERR_WORKSPACE_TOO_SMALL = 3,
+  OC_ERR_NOT_PREPARED = 4,
+  OC_ERR_HIP = 5
+} oc_status;
+
+typedef enum oc_dtype { OC_BF16 = 0, OC_FP16 = 1 } oc_dtype;
+
+typedef struct oc_attn_desc {
+  int32_t B, S, H, D;          /* batch, sequence length, heads, head dim (must be 128) */
+  int32_t dtype;               /* oc_dtype of q, k and v */
+  int64_t stride_b;            /* element strides of q, k, v; channel stride is 1 */
+  int64_t stride_s;
+  int64_t stride_h;
+  float softmax_scale;         /* tau; 0 selects 1/sqrt(D) */
+} oc_attn_desc;
+
+/* Byte offsets of the buffers inside a workspace (all 256-byte aligned), and
+ * the tile counts. Exposed so that tests can read the prepared FP8 tensors. Layouts:
+ *   qhat   u8  [B][H][s_pad_q][128]        natural order, padding rows 0
+ *   kpack  u8  [B][H][n_ktiles][128][128]  key rows; the 16-byte chunk c of
+ *                                          row r is stored at chunk c ^ (r & 7)
+ *   vpack  u8  [B][H][n_ktiles][128][128]  rows are channels d; the key of a
+ *                                          tile at position j sits at column
+ *                                          kk = 32*((j>>2)&3) + 4*(j>>4) + (j&3),
+ *                                          chunk c of row d at chunk c ^ (d & 7)
+ *   sq     f32 [B][H][s_pad_q/128]    sk, vamax f32 [B][H][n_ktiles]
+ *   sv     f32 [B][H][2]              {amax/448, 448/amax} of the head's V
+ *   energy f64 [B][H][S]              residual energy (repair only)
+ *   sel    i32 [B][H][n_sel]          selected tokens, ascending
+ *   kselpack, rpack: like kpack/vpack over the selected tokens (slot order),
+ *                                     [B][H][n_sel_tiles][128][128]
+ *   sksel  f32 [B][H][n_sel_tiles*128]  K block scale of each selected token
+ *   (the repair buffers are packed with the n_sel = ceil(budget*S) and
+ *    n_sel_tiles = ceil(n_sel/128) of the last prepare_v_repair, inside
+ *    space sized for the plan's maximum budget)
+ *   sr     f32 [B][H][2]              {amax/448, 448/amax} of the selected residuals
+ */
+typedef struct oc_attn_ws_layout {
+  uint64_t qhat, kpack, vpack, sq, sk, vamax, sv;
+  uint64_t energy, sel, kselpack, rpack, sksel, sr;
+  uint64_t total_bytes;
+  int32_t n_ktiles, n_qtiles, s_pad_q, n_sel_max, n_sel_tiles_max;
+} oc_attn_ws_layout;
+
+typedef struct oc_attn_plan oc_attn_plan;
+
+/* Create a plan for one problem shape. max_repair_budget in [0, 1] sizes the
+ * repair buffers (0 = no repair). Host-only; makes no HIP call. */
+oc_status oc_attn_plan_create(const oc_attn_desc* desc, double max_repair_budget, oc_attn_plan** plan);
+/* Release a plan (and its cached graph). NULL is ignored. */
+void oc_attn_plan_destroy(oc_attn_plan* plan);
+/* Workspace bytes the plan needs (host-only). */
+oc_status oc_attn_workspace_size(const oc_attn_plan* plan, size_t* bytes);
+/* Buffer offsets inside the workspace (host-only). */
+oc_status oc_attn_workspace_layout(const oc_attn_plan* plan, oc_attn_ws_layout* layout);
+
+/* Quantize q, k, v into the workspace: per-block Q/K scales and E4M3 codes,
+ * per-head V scale and codes packed transposed for the matrix cores. The
+ * prepare kernels run as one captured hipGraph. */
+oc_status oc_attn_prepare(oc_attn_plan* plan, const void* q, const void* k, const void* v,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* Full call: oc_attn_prepare, then ExpCast attention into out (BF16). */
+oc_status oc_attn_forward(oc_attn_plan* plan, const void* q, const void* k, const void* v,
+                          void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* oc_attn_prepare plus the repair set for `budget` (0 <= budget <= the plan's
+ * max): residual energy of every value token, the top ceil(budget*S) tokens
+ * per (b, h) (ties to the lower index), and their E4M3 residuals. */
+oc_status oc_attn_prepare_v_repair(oc_attn_plan* plan, const void* q, const void* k, const void* v,
+                                   double budget, void* ws, size_t ws_bytes, void* stream);
+
+/* Full call with repair: oc_attn_prepare_v_repair, then attention whose
+ * output adds the repaired residuals with the unrepaired row sums. */
+oc_status oc_attn_forward_v_repair(oc_attn_plan* plan, const void* q, const void* k, const void* v,
+                                   double budget, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Attention only, on a workspace this plan prepared earlier (kernel-alone
+ * timing; the plan remembers its 8 most recently prepared workspaces).
+ * with_repair != 0 requires the workspace to come from
+ * oc_attn_prepare_v_repair; its repair set is then applied. */
+oc_status oc_attn_forward_prepared(oc_attn_plan* plan, const void* ws, size_t ws_bytes, void* out,
+                                   int with_repair, void* stream);
+
+/* Parity aid: run the attention kernel on the prepared workspace for the one
+ * (b, h) pair and dump, for every query row < S, the ExpCast byte it wrote
+ * for every key (codes: device u8 [S][S]) and the running row max it used for
+ * each key tile (m_used: device i32 [S][n_ktiles], indexed by tile number).
+ * out receives the normal output for that (b, h). Only for S <= 8192;
+ * larger S gives OC_ERR_UNSUPPORTED. */
+oc_status oc_attn_debug_pcodes(oc_attn_plan* plan, const void* ws, size_t ws_bytes, int32_t b, int32_t h,
+                               uint8_t* codes, int32_t* m_used, void* out, void* stream);
+
+/* Static description of a status code. */
+const char* oc_attn_status_string(oc_status status);
+/* hipError_t of the calling thread's last OC_ERR_HIP (0 if none). */
+int oc_attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OC_ATTN_H */

@@ -26,7 +26,11 @@ Readings where the pages leave a step open (each is listed in the design doc):
     code is 8*(x - M) + 120 + beta; the largest weight lands on code 120.
   * the byte is the round-to-nearest-even of that affine value, clamped to the
     finite codes [0, 126]; keys beyond S get no code.
-  * M is the bit-aligned row max: M = ceil(max_j x_j), an integer.
+  * M is the bit-aligned row max: M = ceil(max_j x_j), an integer. The
+    two-pass form (expcast_attention_head) uses the final M for every key;
+    the single-pass form (expcast_attention_online) follows the kernel the
+    pages describe: key tiles of 128 from the middle of the key window
+    outwards, bytes relative to the running M, exact power-of-two rescales.
   * the row sum is over the decoded weights: L = sum_j dec(c_j).
   * Q/K scale blocks are 128 tokens x 128 channels; scale s = amax/448 in fp32,
     quantization multiplies by the fp32 reciprocal 448/amax; an all-zero
@@ -233,6 +237,72 @@ def expcast_attention_head(q, k, v, tau=None, rows=None, budget=0.0, ph=None,
             acc += float(rp.sr) * (P[:, rp.sel] @ decode(rp.rc))
         out[c0:c0 + len(r)] = acc / L[:, None]
         Ms[c0:c0 + len(r)] = M
+        Ls[c0:c0 + len(r)] = L
+    return {"out": out, "M": Ms, "L": Ls, "ph": ph}
+
+
+def key_tile_order(n_tiles: int) -> list:
+    """Order in which the online form visits the 128-key tiles: from the
+    middle of the key window outwards, c, c-1, c+1, c-2, c+2, ... with
+    c = (n_tiles-1)//2, continuing on the longer side once the shorter one
+    is used up (Open VC Attention product page, kernel paragraph; Open-VC
+    news, "Архитектурные оптимизации")."""
+    c = (n_tiles - 1) // 2
+    order = [c]
+    for d in range(1, n_tiles):
+        if c - d >= 0:
+            order.append(c - d)
+        if c + d < n_tiles:
+            order.append(c + d)
+    return order
+
+
+def expcast_attention_online(q, k, v, tau=None, rows=None, budget=0.0, ph=None, order="mid", chunk=256):
+    """Single-pass (flash) form of ExpCast attention, as the pages' kernel runs
+    it: keys are consumed in 128-key tiles in `order` ("mid" = key_tile_order,
+    "ascending" = 0, 1, 2, ...). Per row, a running bit-aligned max M is raised
+    to ceil(max logit of the tile) before that tile's bytes are written, so
+    bytes are relative to the running max. The partial sums O and L are
+    carried across tiles and multiplied by the exact power of two
+    2^(M_old - M_new) whenever M grows. The repair residuals use the final M.
+
+    It equals expcast_attention_head except for keys whose byte relative to
+    the final max would fall below the normal E4M3 range (the underflow tail):
+    those are kept more precisely when they were visited before the max.
+    """
+    S, D = k.shape
+    tau = 1.0 / math.sqrt(D) if tau is None else tau
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    if ph is None:
+        ph = prepare_head(q, k, v, budget)
+    nT = (S + QK_BLOCK - 1) // QK_BLOCK
+    tiles = key_tile_order(nT) if order == "mid" else list(range(nT))
+    vd = decode(ph.vc)
+    out = np.empty((len(rows), D))
+    Ms = np.empty(len(rows), dtype=np.int64)
+    Ls = np.empty(len(rows))
+    for c0 in range(0, len(rows), chunk):
+        r = rows[c0:c0 + chunk]
+        x = log2_logits(ph, r, tau)
+        M = np.full(len(r), -np.inf)
+        O = np.zeros((len(r), D))
+        L = np.zeros(len(r))
+        for t in tiles:
+            ks = slice(t * QK_BLOCK, min(S, (t + 1) * QK_BLOCK))
+            xt = x[:, ks]
+            Mn = np.maximum(M, np.ceil(xt.max(axis=1)))
+            f = np.where(np.isinf(M), 0.0, np.exp2(M - Mn))     # exact powers of two
+            P = VALUES[expcast_codes(xt, Mn)]
+            O = O * f[:, None] + P @ vd[ks]
+            L = L * f + P.sum(axis=1)
+            M = Mn
+        O *= float(ph.sv)
+        if ph.repair is not None and ph.repair.k > 0:
+            rp = ph.repair
+            P = VALUES[expcast_codes(x[:, rp.sel], M)]
+            O += float(rp.sr) * (P @ decode(rp.rc))
+        out[c0:c0 + len(r)] = O / L[:, None]
+        Ms[c0:c0 + len(r)] = M.astype(np.int64)
         Ls[c0:c0 + len(r)] = L
     return {"out": out, "M": Ms, "L": Ls, "ph": ph}
 

@@ -1,0 +1,147 @@
+"""Boundary tests that need no GPU: the library loads, exports every entry
+point the header declares, sizes workspaces, and rejects bad arguments
+before any HIP call (so every error path is reachable on a CPU-only host)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import bit_fp8_attention_block_amd as oc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "oc_attn.h")
+lib = oc._lib
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(oc_attn_\w+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = header_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(oc.EXPORTS)
+
+
+def make_desc(B=1, S=1000, H=4, D=128, dtype=oc.OC_BF16, strides=None, scale=0.0):
+    strides = strides or (S * H * 128, H * 128, 128)
+    return oc.Desc(B, S, H, D, dtype, strides[0], strides[1], strides[2], scale)
+
+
+def create(desc, budget=0.0):
+    p = ctypes.c_void_p()
+    st = lib.oc_attn_plan_create(ctypes.byref(desc), ctypes.c_double(budget), ctypes.byref(p))
+    return st, p
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=64), oc.OC_ERR_UNSUPPORTED),
+    (dict(dtype=7), oc.OC_ERR_UNSUPPORTED),
+    (dict(B=0), oc.OC_ERR_INVALID_ARGUMENT),
+    (dict(S=0), oc.OC_ERR_INVALID_ARGUMENT),
+    (dict(H=-1), oc.OC_ERR_INVALID_ARGUMENT),
+    (dict(strides=(4000 * 128, 4 * 128, 100)), oc.OC_ERR_INVALID_ARGUMENT),
+    (dict(strides=(4000 * 128, -512, 128)), oc.OC_ERR_INVALID_ARGUMENT),
+    (dict(scale=math.nan), oc.OC_ERR_INVALID_ARGUMENT),
+    (dict(scale=-1.0), oc.OC_ERR_INVALID_ARGUMENT),
+])
+def test_plan_create_rejects(kw, status):
+    st, p = create(make_desc(**kw))
+    assert st == status and not p.value
+
+
+@pytest.mark.parametrize("budget", [-0.1, 1.01, math.nan])
+def test_plan_create_rejects_budget(budget):
+    st, p = create(make_desc(), budget)
+    assert st == oc.OC_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_size_and_layout():
+    B, S, H = 2, 73397, 3
+    st, p = create(make_desc(B=B, S=S, H=H), 0.02)
+    assert st == oc.OC_OK
+    n = ctypes.c_size_t()
+    assert lib.oc_attn_workspace_size(p, ctypes.byref(n)) == oc.OC_OK
+    L = oc.WsLayout()
+    assert lib.oc_attn_workspace_layout(p, ctypes.byref(L)) == oc.OC_OK
+    nT, nQT = math.ceil(S / 128), math.ceil(S / 256)
+    assert (L.n_ktiles, L.n_qtiles, L.s_pad_q) == (nT, nQT, nQT * 256)
+    assert L.n_sel_max == 1468 and L.n_sel_tiles_max == 12
+    offs = [L.qhat, L.kpack, L.vpack, L.sq, L.sk, L.vamax, L.sv, L.energy, L.sel, L.kselpack, L.rpack, L.sksel, L.sr]
+    assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
+    assert L.kpack - L.qhat >= B * H * nQT * 256 * 128
+    assert L.vpack - L.kpack >= B * H * nT * 16384
+    assert L.total_bytes == n.value >= L.sr + B * H * 8
+    lib.oc_attn_plan_destroy(p)
+    st, p = create(make_desc(B=B, S=S, H=H), 0.0)
+    L0 = oc.WsLayout()
+    lib.oc_attn_workspace_layout(p, ctypes.byref(L0))
+    assert L0.n_sel_max == 0 and L0.total_bytes < L.total_bytes
+    lib.oc_attn_plan_destroy(p)
+
+
+FAKE = 1 << 40          # never dereferenced: every call below fails validation first
+
+
+def vp(x):
+    return ctypes.c_void_p(x)
+
+
+def test_forward_argument_errors_before_any_hip_call():
+    st, p = create(make_desc(S=1000, H=4), 0.01)
+    assert st == oc.OC_OK
+    n = ctypes.c_size_t()
+    lib.oc_attn_workspace_size(p, ctypes.byref(n))
+    ws_bytes = n.value
+    q, k, v = FAKE, FAKE + (1 << 30), FAKE + (2 << 30)
+    ws, out = FAKE + (4 << 30), FAKE + (8 << 30)
+    fwd = lib.oc_attn_forward
+    assert fwd(p, None, vp(k), vp(v), vp(out), vp(ws), ws_bytes, None) == oc.OC_ERR_INVALID_ARGUMENT
+    assert fwd(p, vp(q + 8), vp(k), vp(v), vp(out), vp(ws), ws_bytes, None) == oc.OC_ERR_INVALID_ARGUMENT
+    assert fwd(p, vp(q), vp(k), vp(v), vp(out), vp(ws + 16), ws_bytes, None) == oc.OC_ERR_INVALID_ARGUMENT
+    assert fwd(p, vp(q), vp(k), vp(v), vp(out), vp(ws), ws_bytes - 1, None) == oc.OC_ERR_WORKSPACE_TOO_SMALL
+    # out overlapping an input or the workspace
+    assert fwd(p, vp(q), vp(k), vp(v), vp(k + 256), vp(ws), ws_bytes, None) == oc.OC_ERR_INVALID_ARGUMENT
+    assert fwd(p, vp(q), vp(k), vp(v), vp(ws + 1024), vp(ws), ws_bytes, None) == oc.OC_ERR_INVALID_ARGUMENT
+    # workspace overlapping an input
+    assert fwd(p, vp(q), vp(k), vp(v), vp(out), vp(q), ws_bytes, None) == oc.OC_ERR_INVALID_ARGUMENT
+    assert fwd(None, vp(q), vp(k), vp(v), vp(out), vp(ws), ws_bytes, None) == oc.OC_ERR_INVALID_ARGUMENT
+    rep = lib.oc_attn_forward_v_repair
+    for b in (-0.5, 1.5, math.nan, 0.02):    # 0.02 exceeds the plan's 0.01
+        assert rep(p, vp(q), vp(k), vp(v), ctypes.c_double(b), vp(out), vp(ws), ws_bytes, None) == \
+            oc.OC_ERR_INVALID_ARGUMENT
+    prep = lib.oc_attn_prepare_v_repair
+    assert prep(p, vp(q), vp(k), vp(v), ctypes.c_double(2.0), vp(ws), ws_bytes, None) == oc.OC_ERR_INVALID_ARGUMENT
+    assert lib.oc_attn_prepare(p, vp(q), vp(k), vp(v), vp(ws), 100, None) == oc.OC_ERR_WORKSPACE_TOO_SMALL
+    # attention on a workspace this plan never prepared
+    assert lib.oc_attn_forward_prepared(p, vp(ws), ws_bytes, vp(out), 0, None) == oc.OC_ERR_NOT_PREPARED
+    assert lib.oc_attn_forward_prepared(p, vp(ws), ws_bytes, vp(out), 1, None) == oc.OC_ERR_NOT_PREPARED
+    assert lib.oc_attn_forward_prepared(p, vp(ws), 10, vp(out), 0, None) == oc.OC_ERR_WORKSPACE_TOO_SMALL
+    codes, m = FAKE + (16 << 30), FAKE + (20 << 30)
+    assert lib.oc_attn_debug_pcodes(p, vp(ws), ws_bytes, 0, 0, vp(codes), vp(m), vp(out), None) == \
+        oc.OC_ERR_NOT_PREPARED
+    assert lib.oc_attn_debug_pcodes(p, vp(ws), ws_bytes, 0, 9, vp(codes), vp(m), vp(out), None) == \
+        oc.OC_ERR_INVALID_ARGUMENT
+    lib.oc_attn_plan_destroy(p)
+    lib.oc_attn_plan_destroy(None)
+
+
+def test_debug_dump_limited_to_small_s():
+    st, p = create(make_desc(S=9000, H=1))
+    n = ctypes.c_size_t()
+    lib.oc_attn_workspace_size(p, ctypes.byref(n))
+    assert lib.oc_attn_debug_pcodes(p, vp(FAKE), n.value, 0, 0, vp(FAKE + (1 << 34)), vp(FAKE + (1 << 35)),
+                                    vp(FAKE + (1 << 36)), None) == oc.OC_ERR_UNSUPPORTED
+    lib.oc_attn_plan_destroy(p)
+
+
+def test_status_strings():
+    for s in range(6):
+        assert lib.oc_attn_status_string(s)
+    assert lib.oc_attn_last_hip_error() == 0

@@ -1,0 +1,77 @@
+"""Prepare kernels vs the oracle, bit-exact: Q/K block codes and scales, V
+head codes and scale (after undoing the pack layouts), padding left zero."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import WsView, head64, log
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_prepared(q, k, v, prep):
+    w = WsView(prep)
+    B, S, H, _ = q.shape
+    for b in range(B):
+        for h in range(H):
+            ph = oracle.prepare_head(head64(q, b, h), head64(k, b, h), head64(v, b, h))
+            qc = w.qcodes(b, h)
+            assert np.array_equal(qc[:S], ph.qc), (b, h, "q codes")
+            assert not qc[S:].any(), "q padding rows must be zero"
+            sq = w.sq(b, h)
+            assert np.array_equal(sq[:len(ph.sq)], ph.sq), (b, h, "q scales")
+            assert np.all(sq[len(ph.sq):] == 1.0)
+            assert np.array_equal(w.kcodes(b, h), ph.kc), (b, h, "k codes")
+            assert np.array_equal(w.sk(b, h), ph.sk), (b, h, "k scales")
+            assert np.array_equal(w.vcodes(b, h), ph.vc), (b, h, "v codes")
+            s, inv = w.sv(b, h)
+            assert s == ph.sv, (b, h, "v scale")
+            _, inv_o = oracle.quant_scale(np.abs(head64(v, b, h)).max())
+            assert inv == inv_o
+            # padding keys of the last tile are zero in both packs
+            nT = w.L.n_ktiles
+            if S % 128:
+                from gpu_util import unpack_k, unpack_v
+                n = nT * 16384
+                kr = w._arr(w.L.kpack + w.bh(b, h) * n, np.uint8, n)
+                assert not unpack_k(kr, nT * 128)[S:].any()
+                assert not unpack_v(w.vraw(b, h), nT * 128)[S:].any()
+
+
+@pytest.mark.parametrize("case", ["s1024_h2", "ragged_fp16", "strided", "tiny"])
+def test_prepare_bit_exact(case):
+    import bit_fp8_attention_block_amd as oc
+    log(f"[prepare] case={case}")
+    if case == "s1024_h2":
+        q, k, v = workloads.make_inputs("s1024_h2", device="cuda")
+    elif case == "ragged_fp16":
+        q, k, v = workloads.make_inputs("b2_s70000_h40_fp16", device="cuda", S=300, H=3)
+    elif case == "strided":
+        qkv = torch.randn(2, 520, 3, 2, 128, device="cuda").mul_(3).to(torch.bfloat16)
+        q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    else:
+        q, k, v = workloads.random_qkv(1, 1, 1, seed=3, device="cuda")
+    prep = oc.prepare(q, k, v)
+    torch.cuda.synchronize()
+    _check_prepared(q, k, v, prep)
+
+
+def test_prepare_extreme_ranges():
+    """Blocks spanning the whole bf16 range, all-zero blocks, values that land
+    on E4M3 subnormals and exact ties."""
+    import bit_fp8_attention_block_amd as oc
+    log("[prepare] extreme ranges")
+    S, H = 512, 2
+    g = torch.Generator(device="cuda").manual_seed(11)
+    x = torch.randn(1, S, H, 128, device="cuda", generator=g)
+    x = x * torch.exp2(torch.randint(-30, 30, (1, S, H, 1), device="cuda", generator=g).float())
+    q = x.to(torch.bfloat16)
+    k = (x * 1e-3).to(torch.bfloat16)
+    k[:, 128:256] = 0           # an all-zero block: scale 1, codes 0
+    v = torch.randn(1, S, H, 128, device="cuda", generator=g).to(torch.bfloat16)
+    v[0, 5, 0, :] = 1e4          # one huge value sets the head scale, most codes go subnormal
+    prep = oc.prepare(q, k, v)
+    torch.cuda.synchronize()
+    _check_prepared(q, k, v, prep)

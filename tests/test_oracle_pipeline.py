@@ -168,3 +168,103 @@ def test_error_vs_exact_on_small_workload():
         ex = oracle.exact_attention_head(qh, kh, vh, rows=rows)
         errs.append(oracle.rel_l2(o, ex))
     assert all(0.04 < e < 0.07 for e in errs), errs
+
+
+# ---- the single-pass (online) form --------------------------------------
+
+def brute_force_online(q, k, v, order, tau=TAU):
+    """Online ExpCast attention with explicit loops: key tiles of 128 in the
+    given order, running integer max raised before each tile's bytes, running
+    sums multiplied by 2**(M_old - M_new)."""
+    S, D = len(k), len(k[0])
+    qc, kc, sq, sk = [None] * S, [None] * S, [0.0] * S, [0.0] * S
+    for x, codes, sc in ((q, qc, sq), (k, kc, sk)):
+        for b0 in range(0, S, 128):
+            blk = range(b0, min(S, b0 + 128))
+            s, inv = _scales(max(abs(x[i][c]) for i in blk for c in range(D)))
+            for i in blk:
+                codes[i] = [_enc(float(np.float32(x[i][c]) * inv)) for c in range(D)]
+                sc[i] = float(s)
+    sv, invv = _scales(max(abs(v[i][c]) for i in range(S) for c in range(D)))
+    vd = [[_dec(_enc(float(np.float32(v[i][c]) * invv))) for c in range(D)] for i in range(S)]
+    out = []
+    for i in range(S):
+        M, L, O = None, 0.0, [0.0] * D
+        for t in order:
+            keys = range(128 * t, min(S, 128 * t + 128))
+            xs = {}
+            for j in keys:
+                dot = sum(_dec(qc[i][c]) * _dec(kc[j][c]) for c in range(D))
+                xs[j] = tau * LOG2E * dot * (sq[i] * sk[j])
+            Mt = math.ceil(max(xs.values()))
+            if M is None or Mt > M:
+                f = 0.0 if M is None else 2.0 ** (M - Mt)
+                L, O = L * f, [o * f for o in O]
+                M = Mt
+            for j in keys:
+                w = _dec(min(126, max(0, round(8 * (xs[j] - M) + 120 - 0.35))))
+                L += w
+                for c in range(D):
+                    O[c] += w * vd[j][c]
+        out.append([float(sv) * o / L for o in O])
+    return np.array(out)
+
+
+def test_key_tile_order_is_mid_window():
+    assert oracle.key_tile_order(1) == [0]
+    assert oracle.key_tile_order(2) == [0, 1]
+    assert oracle.key_tile_order(5) == [2, 1, 3, 0, 4]
+    assert oracle.key_tile_order(6) == [2, 1, 3, 0, 4, 5]
+    for n in (1, 7, 64, 574):
+        assert sorted(oracle.key_tile_order(n)) == list(range(n))
+
+
+@pytest.mark.parametrize("S", [130, 300])
+def test_online_brute_force_matches_vectorized(S):
+    q, k, v = (t[0, :, 0].double().numpy() for t in workloads.random_qkv(1, S, 1, seed=S + 1, scale=2.0))
+    # a strong key late in the order so the running max has to grow
+    k[S - 1] = q[3] * 1.5
+    k = torch.from_numpy(k).bfloat16().double().numpy()
+    rows = [0, 3, 77, S - 1]
+    nT = -(-S // 128)
+    for order, name in ((oracle.key_tile_order(nT), "mid"), (list(range(nT)), "ascending")):
+        want = brute_force_online(q.tolist(), k.tolist(), v.tolist(), order)[rows]
+        got = oracle.expcast_attention_online(q, k, v, rows=rows, order=name)["out"]
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+def test_online_equals_two_pass_when_max_is_visited_first():
+    """If every row's largest logit lies in the first tile visited, all bytes
+    are written against the final max and both forms coincide."""
+    S = 700
+    rng = np.random.default_rng(4)
+    q = rng.normal(0, 1, (S, 128))
+    k = rng.normal(0, 1, (S, 128))
+    c = oracle.key_tile_order(-(-S // 128))[0]
+    q[:, 0] += 6.0
+    k[c * 128 + 7, 0] = 30.0          # the dominant key sits in the middle tile
+    v = rng.normal(0, 1, (S, 128))
+    q, k, v = (torch.from_numpy(t).bfloat16().double().numpy() for t in (q, k, v))
+    rows = np.arange(0, S, 5)
+    a = oracle.expcast_attention_online(q, k, v, rows=rows)
+    b = oracle.expcast_attention_head(q, k, v, rows=rows)
+    np.testing.assert_array_equal(a["M"], b["M"])
+    np.testing.assert_allclose(a["L"], b["L"], rtol=1e-13)
+    np.testing.assert_allclose(a["out"], b["out"], rtol=1e-12, atol=1e-14)
+
+
+def test_online_and_two_pass_differ_only_through_the_underflow_tail():
+    """Relative to the final max, weights that land in the normal E4M3 range
+    are identical in both forms; the forms differ by at most the tail."""
+    q, k, v = workloads.make_inputs("s8192_h8", S=2048, H=1)
+    qh, kh, vh = (t[0, :, 0].double().numpy() for t in (q, k, v))
+    rows = np.arange(0, 2048, 64)
+    a = oracle.expcast_attention_online(qh, kh, vh, rows=rows, order="ascending")
+    b = oracle.expcast_attention_head(qh, kh, vh, rows=rows)
+    np.testing.assert_array_equal(a["M"], b["M"])
+    x = oracle.log2_logits(b["ph"], rows, TAU)
+    tail = np.where(x - b["M"][:, None] < -14.0, np.exp2(x - b["M"][:, None] + 8), 0.0).sum(axis=1)
+    vmax = float(b["ph"].sv) * np.abs(oracle.decode(b["ph"].vc)).max()
+    bound = 2.0 * tail * vmax / b["L"]            # |dO| <= (tail mass difference) * max|v| / L, both forms
+    dO = np.abs(a["out"] - b["out"]).max(axis=1)
+    assert np.all(dO <= bound + 1e-12)
