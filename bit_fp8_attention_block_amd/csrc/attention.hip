@@ -24,8 +24,9 @@
 //  * the row sum L is one more MFMA per 16 queries against an all-ones A
 //    operand (E4M3 1.0 = 0x38), so the VALU never decodes bytes.
 //  * K and V tiles (16 KiB each) stream through LDS by direct global->LDS
-//    loads (global_load_lds_dwordx4), double-buffered. Their 16-byte
-//    chunks are XOR-swizzled by row so operand reads are conflict-free.
+//    loads (global_load_lds_dwordx4). The prepare step stores them in MFMA
+//    operand order, so every operand read is a contiguous, bank-conflict-
+//    free ds_read_b128.
 //  * row max across the 4 lanes that share a query: v_permlane16/32_swap.
 //  * key tiles are visited from the middle of the key window outwards
 //    (c, c-1, c+1, ... with c = (nT-1)/2; Open VC Attention product page,
@@ -46,10 +47,11 @@ __device__ inline v4f mfma_f8(const v8i& a, const v8i& b, const v4f& c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// 32 operand bytes of `row`, k-slots 32g..32g+31, from a swizzled LDS tile
-__device__ inline v8i lds_operand(const uint8_t* tile, int row, int g) {
-  const uint4 x = *reinterpret_cast<const uint4*>(tile + swz(row, 32 * g));
-  const uint4 y = *reinterpret_cast<const uint4*>(tile + swz(row, 32 * g + 16));
+// The MFMA operand of 16-row block `blk` for this lane: 32 bytes, read as two
+// contiguous 1 KiB wave accesses from an operand-ordered LDS tile
+__device__ inline v8i lds_operand(const uint8_t* tile, int blk, int lane) {
+  const uint4 x = *reinterpret_cast<const uint4*>(tile + ((2 * blk) * 64 + lane) * 16);
+  const uint4 y = *reinterpret_cast<const uint4*>(tile + ((2 * blk + 1) * 64 + lane) * 16);
   v8i r;
   r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
   r[4] = y.x; r[5] = y.y; r[6] = y.z; r[7] = y.w;
@@ -72,16 +74,17 @@ __device__ inline int tile_at(int s, int c, int nT, int order) {
   return left > right ? c - m - extra : c + m + extra;
 }
 
+// One 16 KiB tile from global memory into LDS by direct global->LDS loads:
+// 1024 chunks of 16 bytes; each instruction moves 1 KiB per wave, lane l's
+// chunk landing at wave base + 16*l.
 template <int NT>
-__device__ inline void issue_tile_load(uint8_t* lds_buf, const uint8_t* ktile, const uint8_t* vtile) {
-  // 32 KiB = 2048 chunks of 16 bytes; each instruction moves 1 KiB per wave,
-  // lane l's chunk landing at wave base + 16*l
+__device__ inline void load_tile(uint8_t* lds_dst, const uint8_t* src) {
   const int tid = threadIdx.x, wv = tid >> 6;
 #pragma unroll
-  for (int i = 0; i < 2048 / NT; ++i) {
+  for (int i = 0; i < 1024 / NT; ++i) {
     const int ci = i * NT + tid;
-    const uint8_t* src = (i * NT < 1024) ? ktile + ci * 16 : vtile + (ci - 1024) * 16;
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_buf + (i * NT + wv * 64) * 16),
+    __builtin_amdgcn_global_load_lds(src + ci * 16,
+                                     (__attribute__((address_space(3))) void*)(lds_dst + (i * NT + wv * 64) * 16),
                                      16, 0, 0);
   }
 }
@@ -96,12 +99,159 @@ __device__ inline float max_over_row_lanes(float m) {
   return __builtin_fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
 }
 
-// QBW = 16-query blocks per wave; the workgroup has 16/QBW waves (256 queries)
-template <int QBW, bool REPAIR, bool DUMP>
-__global__ __launch_bounds__(1024 / QBW) void attn_kernel(AttnArgs a) {
-  constexpr int NW = 16 / QBW;
-  constexpr int NT = 64 * NW;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2][2 * TILE_BYTES];
+constexpr int QBW = 2;            // 16-query blocks per wave
+constexpr int NWAVES = 8;         // 2 waves per SIMD: one of each group
+constexpr int NTHREADS = 64 * NWAVES;
+constexpr int LDS_BYTES = 6 * TILE_BYTES;   // K and V, three buffers each
+
+// scheduling-group masks of __builtin_amdgcn_sched_group_barrier
+constexpr int SG_MFMA = 0x008, SG_VALU = 0x002, SG_DS_READ = 0x100;
+
+// S^T = K Q^T for one 128-key tile and the wave's 32 queries. The operand of
+// 16-key block kb+2 is read from LDS while the MFMAs of block kb run, so the
+// LDS latency hides behind 4 MFMAs instead of stalling every pair.
+__device__ __forceinline__ void qk_tile(const uint8_t* kt, const v8i (&qop)[QBW], v4f (&S)[QBW][8], int lane) {
+  v8i kop[8];
+  kop[0] = lds_operand(kt, 0, lane);
+  kop[1] = lds_operand(kt, 1, lane);
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb) {
+    if (kb + 2 < 8) kop[kb + 2] = lds_operand(kt, kb + 2, lane);
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb) S[qb][kb] = mfma_f8(kop[kb], qop[qb], v4f{0.f, 0.f, 0.f, 0.f});
+  }
+  __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
+#pragma unroll
+  for (int kb = 0; kb < 6; ++kb) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, QBW, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2 * QBW, 0);
+}
+
+// O^T += V^T P^T and L += 1 * P^T for one tile, with the same read-ahead
+__device__ __forceinline__ void pv_tile(const uint8_t* vt, const v8i (&P)[QBW], v4f (&O)[QBW][8], v4f (&L)[QBW],
+                                        int lane) {
+  v8i ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = 0x38383838;   // E4M3 1.0
+  v8i vop[8];
+  vop[0] = lds_operand(vt, 0, lane);
+  vop[1] = lds_operand(vt, 1, lane);
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    if (n + 2 < 8) vop[n + 2] = lds_operand(vt, n + 2, lane);
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb) O[qb][n] = mfma_f8(vop[n], P[qb], O[qb][n]);
+  }
+#pragma unroll
+  for (int qb = 0; qb < QBW; ++qb) L[qb] = mfma_f8(ones, P[qb], L[qb]);
+  __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
+#pragma unroll
+  for (int n = 0; n < 6; ++n) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, QBW, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(SG_MFMA, 3 * QBW, 0);
+}
+
+// max of the 32 scores a lane holds for one 16-query block, as a tree of
+// v_max3 so the dependent chain is 4 deep instead of 16
+__device__ __forceinline__ float lane_max32(const v4f (&Sc)[8]) {
+  float t[8];
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb)
+    t[kb] = __builtin_fmaxf(__builtin_fmaxf(Sc[kb][0], Sc[kb][1]), __builtin_fmaxf(Sc[kb][2], Sc[kb][3]));
+  const float a = __builtin_fmaxf(__builtin_fmaxf(t[0], t[1]), t[2]);
+  const float b = __builtin_fmaxf(__builtin_fmaxf(t[3], t[4]), t[5]);
+  return __builtin_fmaxf(__builtin_fmaxf(a, b), __builtin_fmaxf(t[6], t[7]));
+}
+
+// ExpCast for one tile and the wave's two 16-query blocks: raise the running
+// bit-aligned max (rescaling O and L by the exact power of two when it
+// grows), then one FMA and one saturating convert per score give the E4M3
+// bytes. Both blocks are handled side by side to give the VALU independent
+// work, with one (rarely taken) rescale branch.
+template <bool DUMP>
+__device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], const float (&aq)[QBW], float skj,
+                                             float (&M)[QBW], v4f (&O)[QBW][8], v4f (&L)[QBW], int j, bool masked,
+                                             const AttnArgs& a, int g, int qrow0) {
+  if (masked) {
+    // keys beyond S in the last (ragged) tile take no part in max or sums
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool dead = j * KTILE + 16 * kb + 4 * g + r >= a.S;
+#pragma unroll
+        for (int qb = 0; qb < QBW; ++qb)
+          if (dead) S[qb][kb][r] = -__builtin_inff();
+      }
+  }
+  float aqs[QBW], Mn[QBW];
+  bool grow = false;
+#pragma unroll
+  for (int qb = 0; qb < QBW; ++qb) {
+    aqs[qb] = aq[qb] * skj;
+    const float m = max_over_row_lanes(lane_max32(S[qb]));
+    Mn[qb] = __builtin_fmaxf(M[qb], __builtin_ceilf((aqs[qb] * m) * 0.125f));
+    grow |= Mn[qb] > M[qb];
+  }
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb) {
+      const int d = (int)(M[qb] - Mn[qb]);   // <= 0
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) O[qb][n][r] = __builtin_ldexpf(O[qb][n][r], d);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) L[qb][r] = __builtin_ldexpf(L[qb][r], d);
+      M[qb] = Mn[qb];
+    }
+  }
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb) {
+      const float bq = __builtin_fmaf(-8.0f, Mn[qb], EXPCAST_C);
+      uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(S[qb][kb][0], aqs[qb], bq), 0, 0u);
+      w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(S[qb][kb][1], aqs[qb], bq), 1, w);
+      w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(S[qb][kb][2], aqs[qb], bq), 2, w);
+      w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(S[qb][kb][3], aqs[qb], bq), 3, w);
+      P[qb][kb] = (int)w;
+    }
+  if (DUMP) {
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb) {
+      const int qrow = qrow0 + 16 * qb;
+      if (qrow < a.S) {
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = j * KTILE + 16 * kb + 4 * g + r;
+            if (key < a.S) a.dump_codes[(int64_t)qrow * a.S + key] = (uint8_t)((uint32_t)P[qb][kb] >> (8 * r));
+          }
+        if (g == 0) a.dump_m[(int64_t)qrow * a.nT + j] = (int32_t)Mn[qb];
+      }
+    }
+  }
+}
+
+// One workgroup = 256 queries of one (b, h): 8 waves of 32 queries. Waves
+// 0-3 (group A) and 4-7 (group B) share the SIMDs pairwise and run the
+// same tile loop half an iteration apart, so that on every SIMD one wave
+// issues MFMAs while the other runs the VALU part:
+//   group A, iteration s:  ExpCast(s) | PV(s), QK(s+1)
+//   group B, iteration s:  PV(s-1), QK(s) | ExpCast(s)
+// Iteration s reads K tiles s and s+1 and V tiles s-1 and s while K s+2 and
+// V s+1 stream in, so K and V are triple-buffered in LDS (96 KiB).
+template <bool REPAIR, bool DUMP>
+__global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  uint8_t* const kbuf = smem;
+  uint8_t* const vbuf = smem + 3 * TILE_BYTES;
 
   int b, h, qt;
   if (DUMP) {
@@ -120,7 +270,9 @@ __global__ __launch_bounds__(1024 / QBW) void attn_kernel(AttnArgs a) {
   }
   const int bh = b * a.H + h;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const bool group_b = a.grouping ? (wv & 1) != 0 : (wv >> 2) != 0;
   const int q0 = qt * BQ + wv * QBW * 16;
+  const int qrow0 = q0 + l16;
   const int nT = a.nT;
 
   // Q^T operands stay in registers for the whole loop
@@ -136,123 +288,55 @@ __global__ __launch_bounds__(1024 / QBW) void attn_kernel(AttnArgs a) {
     aq[qb] = a.c8 * a.sq[(int64_t)bh * a.nQB + ((q0 + 16 * qb) >> 7)];
   }
 
-  v4f O[8][QBW];
-  v4f Lacc[QBW];
+  v4f O[QBW][8], L[QBW], S[QBW][8];
+  v8i P[QBW];
   float M[QBW];
 #pragma unroll
   for (int qb = 0; qb < QBW; ++qb) {
-    Lacc[qb] = v4f{0.f, 0.f, 0.f, 0.f};
+    L[qb] = v4f{0.f, 0.f, 0.f, 0.f};
     M[qb] = -16384.0f;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) O[n][qb] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < 8; ++n) O[qb][n] = v4f{0.f, 0.f, 0.f, 0.f};
   }
-  v8i ones;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = 0x38383838;   // E4M3 1.0
 
-  const uint8_t* kbase = a.kpack + (int64_t)bh * nT * TILE_BYTES;
-  const uint8_t* vbase = a.vpack + (int64_t)bh * nT * TILE_BYTES;
+  const uint8_t* kg = a.kpack + (int64_t)bh * nT * TILE_BYTES;
+  const uint8_t* vg = a.vpack + (int64_t)bh * nT * TILE_BYTES;
   const float* skp = a.sk + (int64_t)bh * nT;
   const int centre = (nT - 1) >> 1;
-  const bool ragged = (a.S & (KTILE - 1)) != 0;
+  const int last_masked = (a.S & (KTILE - 1)) ? nT - 1 : -1;
 
-  {
-    const int j0 = tile_at(0, centre, nT, a.order);
-    issue_tile_load<NT>(smem[0], kbase + (int64_t)j0 * TILE_BYTES, vbase + (int64_t)j0 * TILE_BYTES);
-  }
-  __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0): this wave's tile chunks are in LDS
+  load_tile<NTHREADS>(kbuf, kg + (int64_t)tile_at(0, centre, nT, a.order) * TILE_BYTES);
+  load_tile<NTHREADS>(vbuf, vg + (int64_t)tile_at(0, centre, nT, a.order) * TILE_BYTES);
+  if (nT > 1) load_tile<NTHREADS>(kbuf + TILE_BYTES, kg + (int64_t)tile_at(1, centre, nT, a.order) * TILE_BYTES);
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's chunks are in LDS
   __syncthreads();
+  if (!group_b) qk_tile(kbuf, qop, S, lane);
 
+  int ks = 0;   // buffer index of K tile s (= s % 3)
   for (int s = 0; s < nT; ++s) {
     const int j = tile_at(s, centre, nT, a.order);
-    const int buf = s & 1;
-    if (s + 1 < nT) {
-      const int jn = tile_at(s + 1, centre, nT, a.order);
-      issue_tile_load<NT>(smem[buf ^ 1], kbase + (int64_t)jn * TILE_BYTES, vbase + (int64_t)jn * TILE_BYTES);
-    }
-    const uint8_t* kt = smem[buf];
-    const uint8_t* vt = smem[buf] + TILE_BYTES;
-
-    // ---- S^T = K Q^T for 128 keys x (16*QBW) queries
-    v4f Sc[8][QBW];
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-      const v8i kop = lds_operand(kt, 16 * kb + l16, g);
-#pragma unroll
-      for (int qb = 0; qb < QBW; ++qb) Sc[kb][qb] = mfma_f8(kop, qop[qb], v4f{0.f, 0.f, 0.f, 0.f});
-    }
-    if (ragged && j == nT - 1) {
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool dead = j * KTILE + 16 * kb + 4 * g + r >= a.S;
-#pragma unroll
-          for (int qb = 0; qb < QBW; ++qb)
-            if (dead) Sc[kb][qb][r] = -__builtin_inff();
-        }
-    }
+    const int ks1 = ks == 2 ? 0 : ks + 1, ks2 = ks1 == 2 ? 0 : ks1 + 1;   // s+1, s+2 (and s-1) mod 3
+    if (s + 2 < nT) load_tile<NTHREADS>(kbuf + ks2 * TILE_BYTES, kg + (int64_t)tile_at(s + 2, centre, nT, a.order) * TILE_BYTES);
+    if (s + 1 < nT) load_tile<NTHREADS>(vbuf + ks1 * TILE_BYTES, vg + (int64_t)tile_at(s + 1, centre, nT, a.order) * TILE_BYTES);
     const float skj = skp[j];
-
-    // ---- ExpCast: bytes straight from the scores
-    v8i P[QBW];
-#pragma unroll
-    for (int qb = 0; qb < QBW; ++qb) {
-      float m = Sc[0][qb][0];
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) m = __builtin_fmaxf(m, Sc[kb][qb][r]);
-      m = max_over_row_lanes(m);
-      const float al = aq[qb] * skj;
-      const float mt = __builtin_ceilf((al * m) * 0.125f);
-      const float Mn = __builtin_fmaxf(M[qb], mt);
-      if (__builtin_amdgcn_ballot_w64(Mn > M[qb]) != 0) {
-        const int d = (int)(M[qb] - Mn);   // <= 0
-#pragma unroll
-        for (int n = 0; n < 8; ++n)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) O[n][qb][r] = __builtin_ldexpf(O[n][qb][r], d);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Lacc[qb][r] = __builtin_ldexpf(Lacc[qb][r], d);
-        M[qb] = Mn;
-      }
-      const float bq = __builtin_fmaf(-8.0f, Mn, EXPCAST_C);
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb) {
-        uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(Sc[kb][qb][0], al, bq), 0, 0u);
-        w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(Sc[kb][qb][1], al, bq), 1, w);
-        w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(Sc[kb][qb][2], al, bq), 2, w);
-        w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(Sc[kb][qb][3], al, bq), 3, w);
-        P[qb][kb] = (int)w;
-      }
-      if (DUMP) {
-        const int qrow = q0 + 16 * qb + l16;
-        if (qrow < a.S) {
-#pragma unroll
-          for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int key = j * KTILE + 16 * kb + 4 * g + r;
-              if (key < a.S) a.dump_codes[(int64_t)qrow * a.S + key] = (uint8_t)((uint32_t)P[qb][kb] >> (8 * r));
-            }
-          if (g == 0) a.dump_m[(int64_t)qrow * nT + j] = (int32_t)Mn;
-        }
-      }
+    if (!group_b) {
+      expcast_tile<DUMP>(S, P, aq, skj, M, O, L, j, j == last_masked, a, g, qrow0);
+      pv_tile(vbuf + ks * TILE_BYTES, P, O, L, lane);
+      if (s + 1 < nT) qk_tile(kbuf + ks1 * TILE_BYTES, qop, S, lane);
+    } else {
+      // QK first: its results are ready by the time the PV MFMAs have issued
+      qk_tile(kbuf + ks * TILE_BYTES, qop, S, lane);
+      if (s > 0) pv_tile(vbuf + ks2 * TILE_BYTES, P, O, L, lane);   // V tile s-1 sits in buffer (s+2) % 3
+      expcast_tile<DUMP>(S, P, aq, skj, M, O, L, j, j == last_masked, a, g, qrow0);
     }
-
-    // ---- O^T += V^T P^T ; L += 1 * P^T
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const v8i vop = lds_operand(vt, 16 * n + l16, g);
-#pragma unroll
-      for (int qb = 0; qb < QBW; ++qb) O[n][qb] = mfma_f8(vop, P[qb], O[n][qb]);
-    }
-#pragma unroll
-    for (int qb = 0; qb < QBW; ++qb) Lacc[qb] = mfma_f8(ones, P[qb], Lacc[qb]);
-
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    ks = ks1;
+  }
+  if (group_b) {
+    // V tile nT-1 is in buffer (nT-1) % 3 = (ks + 2) % 3 after the loop
+    const int kl = ks == 0 ? 2 : ks - 1;
+    pv_tile(vbuf + kl * TILE_BYTES, P, O, L, lane);
   }
 
   float scale = a.sv[2 * bh];
@@ -262,24 +346,23 @@ __global__ __launch_bounds__(1024 / QBW) void attn_kernel(AttnArgs a) {
     const float sr = a.sr[2 * bh];
     const float rs = scale / sr;
 #pragma unroll
-    for (int n = 0; n < 8; ++n)
+    for (int qb = 0; qb < QBW; ++qb)
 #pragma unroll
-      for (int qb = 0; qb < QBW; ++qb) O[n][qb] *= rs;
+      for (int n = 0; n < 8; ++n) O[qb][n] *= rs;
     scale = sr;
     const int nslot = a.n_sel_tiles * KTILE;
     const uint8_t* ksb = a.kselpack + (int64_t)bh * a.n_sel_tiles * TILE_BYTES;
     const uint8_t* rsb = a.rpack + (int64_t)bh * a.n_sel_tiles * TILE_BYTES;
     const float* sks = a.sksel + (int64_t)bh * nslot;
     for (int ts = 0; ts < a.n_sel_tiles; ++ts) {
-      issue_tile_load<NT>(smem[0], ksb + (int64_t)ts * TILE_BYTES, rsb + (int64_t)ts * TILE_BYTES);
+      __syncthreads();   // every wave is done with the buffers about to be overwritten
+      load_tile<NTHREADS>(kbuf, ksb + (int64_t)ts * TILE_BYTES);
+      load_tile<NTHREADS>(vbuf, rsb + (int64_t)ts * TILE_BYTES);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      const uint8_t* kt = smem[0];
-      const uint8_t* rt = smem[0] + TILE_BYTES;
-      v8i P[QBW];
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) {
-        const v8i kop = lds_operand(kt, 16 * kb + l16, g);
+        const v8i kop = lds_operand(kbuf, kb, lane);
         float skk[4];
         bool live[4];
 #pragma unroll
@@ -303,11 +386,10 @@ __global__ __launch_bounds__(1024 / QBW) void attn_kernel(AttnArgs a) {
       }
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
-        const v8i rop = lds_operand(rt, 16 * n + l16, g);
+        const v8i rop = lds_operand(vbuf, n, lane);
 #pragma unroll
-        for (int qb = 0; qb < QBW; ++qb) O[n][qb] = mfma_f8(rop, P[qb], O[n][qb]);
+        for (int qb = 0; qb < QBW; ++qb) O[qb][n] = mfma_f8(rop, P[qb], O[qb][n]);
       }
-      __syncthreads();
     }
   }
 
@@ -316,34 +398,35 @@ __global__ __launch_bounds__(1024 / QBW) void attn_kernel(AttnArgs a) {
   for (int qb = 0; qb < QBW; ++qb) {
     const int qrow = q0 + 16 * qb + l16;
     if (qrow >= a.S) continue;
-    const float f = scale / Lacc[qb][0];
+    const float f = scale / L[qb][0];
     uint16_t* orow = a.out + (((int64_t)b * a.S + qrow) * a.H + h) * HEAD_DIM + 4 * g;
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
-      const uint32_t lo = f32_to_bf16(O[n][qb][0] * f) | (f32_to_bf16(O[n][qb][1] * f) << 16);
-      const uint32_t hi = f32_to_bf16(O[n][qb][2] * f) | (f32_to_bf16(O[n][qb][3] * f) << 16);
+      const uint32_t lo = f32_to_bf16(O[qb][n][0] * f) | (f32_to_bf16(O[qb][n][1] * f) << 16);
+      const uint32_t hi = f32_to_bf16(O[qb][n][2] * f) | (f32_to_bf16(O[qb][n][3] * f) << 16);
       *reinterpret_cast<uint2*>(orow + 16 * n) = make_uint2(lo, hi);
     }
   }
 }
 
-template <int QBW>
-static hipError_t launch_q(const AttnArgs& a, bool repair, bool dump, hipStream_t st) {
-  const dim3 block(1024 / QBW);
-  if (dump) {
-    hipLaunchKernelGGL((attn_kernel<QBW, false, true>), dim3(a.nQT), block, 0, st, a);
-  } else {
-    const int nwork = a.B * a.H * a.nQT;
-    const dim3 grid(8 * ((nwork + 7) / 8));
-    if (repair) hipLaunchKernelGGL((attn_kernel<QBW, true, false>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((attn_kernel<QBW, false, false>), grid, block, 0, st, a);
+template <bool REPAIR, bool DUMP>
+static hipError_t launch_one(const AttnArgs& a, dim3 grid, hipStream_t st) {
+  static bool configured = false;
+  if (!configured) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<REPAIR, DUMP>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    if (e != hipSuccess) return e;
+    configured = true;
   }
+  hipLaunchKernelGGL((attn_kernel<REPAIR, DUMP>), grid, dim3(NTHREADS), LDS_BYTES, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_attention(const AttnArgs& a, bool repair, bool dump, int qbw, hipStream_t st) {
-  if (qbw == 2) return launch_q<2>(a, repair, dump, st);
-  return launch_q<4>(a, repair, dump, st);
+hipError_t launch_attention(const AttnArgs& a, bool repair, bool dump, hipStream_t st) {
+  if (dump) return launch_one<false, true>(a, dim3(a.nQT), st);
+  const int nwork = a.B * a.H * a.nQT;
+  const dim3 grid(8 * ((nwork + 7) / 8));
+  return repair ? launch_one<true, false>(a, grid, st) : launch_one<false, false>(a, grid, st);
 }
 
 }  // namespace oc

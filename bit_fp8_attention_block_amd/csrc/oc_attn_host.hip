@@ -46,8 +46,8 @@ struct oc_attn_plan {
   float tau;
   int n_sel_max;
   oc_attn_ws_layout L;
-  int qbw;
   int order;
+  int grouping;
   // cached prepare graph
   hipGraphExec_t gexec = nullptr;
   hipStream_t cap_stream = nullptr;
@@ -221,6 +221,7 @@ static AttnArgs attn_args(const oc_attn_plan* p, const void* ws, void* out, int 
   a.s_pad_q = L.s_pad_q;
   a.c8 = (float)(8.0 * (double)p->tau * 1.4426950408889634);
   a.order = p->order;
+  a.grouping = p->grouping;
   return a;
 }
 
@@ -276,7 +277,7 @@ static oc_status run_prepare(oc_attn_plan* p, const void* q, const void* k, cons
 
 static oc_status run_attention(oc_attn_plan* p, const void* ws, void* out, int n_sel, hipStream_t st) {
   const AttnArgs a = attn_args(p, ws, out, n_sel);
-  const hipError_t e = launch_attention(a, n_sel > 0, false, p->qbw, st);
+  const hipError_t e = launch_attention(a, n_sel > 0, false, st);
   return e == hipSuccess ? OC_OK : hip_fail(e);
 }
 
@@ -302,10 +303,10 @@ oc_status oc_attn_plan_create(const oc_attn_desc* desc, double max_repair_budget
   p->max_budget = max_repair_budget;
   p->tau = d.softmax_scale > 0.0f ? d.softmax_scale : (float)(1.0 / std::sqrt((double)d.D));
   p->n_sel_max = repair_count(max_repair_budget, d.S);
-  const char* qbw = std::getenv("OC_ATTN_QBW");
-  p->qbw = (qbw && std::atoi(qbw) == 2) ? 2 : 4;
   const char* order = std::getenv("OC_ATTN_ORDER");
   p->order = (order && std::atoi(order) == 1) ? 1 : 0;
+  const char* grouping = std::getenv("OC_ATTN_GROUPING");
+  p->grouping = (grouping && std::atoi(grouping) == 1) ? 1 : 0;
   compute_layout(p);
   *plan = p;
   return OC_OK;
@@ -401,7 +402,7 @@ oc_status oc_attn_debug_pcodes(oc_attn_plan* p, const void* ws, size_t ws_bytes,
   a.dump_m = m_used;
   a.dump_b = b;
   a.dump_h = h;
-  const hipError_t e = launch_attention(a, false, true, p->qbw, (hipStream_t)stream);
+  const hipError_t e = launch_attention(a, false, true, (hipStream_t)stream);
   return e == hipSuccess ? OC_OK : hip_fail(e);
 }
 

@@ -23,11 +23,17 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 // ---- pack layouts (workspace format, documented in oc_attn.h) ----
 
-// Byte offset of (row, column) inside a 128x128 FP8 tile whose 16-byte
-// chunks are XOR-swizzled by the row, so that 8 consecutive rows read at
-// the same logical chunk hit 8 different bank groups of LDS.
-__host__ __device__ inline int swz(int row, int col) {
-  return row * 128 + ((((col >> 4) ^ (row & 7))) << 4) + (col & 15);
+// Byte offset of (row, column) inside a 128x128 FP8 tile stored in MFMA
+// operand order. The 16x16x128 FP8 MFMA takes, in lane l, 32 bytes of row
+// l%16 of a 16-row block: columns 32*(l/16) .. +32, as two 16-byte halves.
+// The tile is stored so that the half h of 16-row block kb for lane l is the
+// 16-byte chunk (2*kb + h)*64 + l: an operand read is then one contiguous
+// 1 KiB ds_read_b128 per wave (the only bank-conflict-free b128 pattern on
+// gfx950), and the global->LDS copy of a tile stays a straight copy.
+__host__ __device__ inline int opidx(int row, int col) {
+  const int c = col >> 4;                              // 16-byte chunk of the row
+  const int lane = ((c >> 1) << 4) | (row & 15);
+  return ((((row >> 4) << 1) | (c & 1)) * 64 + lane) * 16 + (col & 15);
 }
 
 // Column of key j (0..127) in a transposed V tile. The QK^T MFMA output leaves

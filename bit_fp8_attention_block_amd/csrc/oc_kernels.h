@@ -46,13 +46,14 @@ struct AttnArgs {
   uint16_t* out;               // bf16 [B][S][H][128], contiguous
   int B, S, H, nT, nQT, nQB, s_pad_q;
   float c8;                    // 8 * tau * log2(e)
-  int order;                   // 0: mid-window (from the query tile outward), 1: ascending
+  int order;                   // 0: from the middle of the key window outwards, 1: ascending
+  int grouping;                // which waves pair up on a SIMD: 0 = w and w+4, 1 = 2i and 2i+1
   uint8_t* dump_codes;         // debug: [S][S] bytes for one (b, h)
   int32_t* dump_m;             // debug: [S][nT]
   int dump_b, dump_h;
 };
 
 hipError_t launch_prepare(const PrepArgs& a, bool fp16, hipStream_t st);
-hipError_t launch_attention(const AttnArgs& a, bool repair, bool dump, int qbw, hipStream_t st);
+hipError_t launch_attention(const AttnArgs& a, bool repair, bool dump, hipStream_t st);
 
 }  // namespace oc

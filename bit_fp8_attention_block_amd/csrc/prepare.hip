@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void prep_qk_kernel(PrepArgs a) {
   for (int p = 0; p < 4; ++p) {
     const int row = 32 * p + rsub;
     *reinterpret_cast<uint4*>(qdst + row * HEAD_DIM + 16 * oc) = encode16<FP16>(ql[p], qh[p], iq);
-    if (kv) *reinterpret_cast<uint4*>(kdst + swz(row, 16 * oc)) = encode16<FP16>(kl[p], kh[p], ik);
+    if (kv) *reinterpret_cast<uint4*>(kdst + opidx(row, 16 * oc)) = encode16<FP16>(kl[p], kh[p], ik);
   }
 }
 
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256) void prep_v_kernel(PrepArgs a) {
       const uint32_t word = (wsel == 0) ? cd[r].x : (wsel == 1) ? cd[r].y : (wsel == 2) ? cd[r].z : cd[r].w;
       w |= ((word >> sh) & 0xFFu) << (8 * r);
     }
-    *reinterpret_cast<uint32_t*>(lds + swz(16 * oc + c, kcol)) = w;
+    *reinterpret_cast<uint32_t*>(lds + opidx(16 * oc + c, kcol)) = w;
   }
   __syncthreads();
   uint8_t* dst = a.vpack + ((int64_t)bh * a.nT + tile) * TILE_BYTES;
@@ -344,12 +344,12 @@ __global__ __launch_bounds__(256) void pack_repair_kernel(PrepArgs a) {
       const int sr = j & 127;
 #pragma unroll
       for (int c = 4 * half; c < 4 * half + 4; ++c)
-        *reinterpret_cast<uint4*>(dst + swz(sl, 16 * c)) = *reinterpret_cast<const uint4*>(src + swz(sr, 16 * c));
+        *reinterpret_cast<uint4*>(dst + opidx(sl, 16 * c)) = *reinterpret_cast<const uint4*>(src + opidx(sr, 16 * c));
       if (half == 0) a.sksel[(int64_t)bh * nslot + slot] = a.sk[(int64_t)bh * a.nT + (j >> 7)];
     } else {
 #pragma unroll
       for (int c = 4 * half; c < 4 * half + 4; ++c)
-        *reinterpret_cast<uint4*>(dst + swz(sl, 16 * c)) = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(dst + opidx(sl, 16 * c)) = make_uint4(0, 0, 0, 0);
       if (half == 0) a.sksel[(int64_t)bh * nslot + slot] = 0.0f;
     }
   }
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(256) void pack_repair_kernel(PrepArgs a) {
     uint32_t w = 0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) w |= ((cw[r][c >> 2] >> (8 * (c & 3))) & 0xFFu) << (8 * r);
-    *reinterpret_cast<uint32_t*>(lds + swz(16 * oc + c, kcol)) = w;
+    *reinterpret_cast<uint32_t*>(lds + opidx(16 * oc + c, kcol)) = w;
   }
   __syncthreads();
   uint8_t* dst = a.rpack + ((int64_t)bh * a.n_sel_tiles + ts) * TILE_BYTES;

@@ -99,12 +99,15 @@ typedef struct oc_attn_desc {
 /* Byte offsets of the buffers inside a workspace (all 256-byte aligned), and
  * the tile counts. Exposed so that tests can read the prepared FP8 tensors. Layouts:
  *   qhat   u8  [B][H][s_pad_q][128]        natural order, padding rows 0
- *   kpack  u8  [B][H][n_ktiles][128][128]  key rows; the 16-byte chunk c of
- *                                          row r is stored at chunk c ^ (r & 7)
- *   vpack  u8  [B][H][n_ktiles][128][128]  rows are channels d; the key of a
- *                                          tile at position j sits at column
- *                                          kk = 32*((j>>2)&3) + 4*(j>>4) + (j&3),
- *                                          chunk c of row d at chunk c ^ (d & 7)
+ *   kpack  u8  [B][H][n_ktiles][16384]     key tiles of 128 keys x 128 channels
+ *                                          in MFMA operand order: columns
+ *                                          32g+16h..+16 of row r (g, h in
+ *                                          0..3, 0..1) form 16-byte chunk
+ *                                          (2*(r/16) + h)*64 + 16g + r%16
+ *   vpack  u8  [B][H][n_ktiles][16384]     transposed value tiles (rows =
+ *                                          channels d, columns = keys), same
+ *                                          chunk order; key j of the tile sits
+ *                                          at column kk = 32*((j>>2)&3) + 4*(j>>4) + (j&3)
  *   sq     f32 [B][H][s_pad_q/128]    sk, vamax f32 [B][H][n_ktiles]
  *   sv     f32 [B][H][2]              {amax/448, 448/amax} of the head's V
  *   energy f64 [B][H][S]              residual energy (repair only)

@@ -27,26 +27,30 @@ def _key_col(j):
     return 32 * ((j >> 2) & 3) + 4 * (j >> 4) + (j & 3)
 
 
+def _opidx(row, col):
+    """byte offset of (row, col) in a 128x128 tile stored in MFMA operand
+    order: chunk c = col // 16 of row r is 16-byte chunk
+    (2*(r//16) + c%2)*64 + 16*(c//2) + r%16 of the tile"""
+    row, col = np.asarray(row), np.asarray(col)
+    c = col >> 4
+    lane = ((c >> 1) << 4) | (row & 15)
+    return ((((row >> 4) << 1) | (c & 1)) * 64 + lane) * 16 + (col & 15)
+
+
 def unpack_k(tiles: np.ndarray, S: int) -> np.ndarray:
     """kpack bytes of one head [nT*16384] -> key codes [S, 128]."""
     nT = tiles.size // 16384
-    t = tiles.reshape(nT, 128, 8, 16)
-    r = np.arange(128)[:, None]
-    c = np.arange(8)[None, :]
-    logical = t[:, r, c ^ (r & 7), :]            # [nT, 128, 8, 16]
-    return logical.reshape(nT * 128, 128)[:S]
+    t = tiles.reshape(nT, 16384)
+    off = _opidx(np.arange(128)[:, None], np.arange(128)[None, :])   # [key, channel]
+    return t[:, off].reshape(nT * 128, 128)[:S]
 
 
 def unpack_v(tiles: np.ndarray, S: int) -> np.ndarray:
     """vpack bytes of one head [nT*16384] -> value codes [S, 128]."""
     nT = tiles.size // 16384
-    t = tiles.reshape(nT, 128, 128)              # [tile, d, physical column]
-    j = np.arange(128)
-    kk = _key_col(j)
-    d = np.arange(128)[:, None]
-    phys = (((kk[None, :] >> 4) ^ (d & 7)) << 4) | (kk[None, :] & 15)   # [d, j]
-    vals = t[:, d, phys]                         # [tile, d, j]
-    return vals.transpose(0, 2, 1).reshape(nT * 128, 128)[:S]
+    t = tiles.reshape(nT, 16384)
+    off = _opidx(np.arange(128)[None, :], _key_col(np.arange(128))[:, None])   # [key, d]
+    return t[:, off].reshape(nT * 128, 128)[:S]
 
 
 class WsView:

@@ -6,27 +6,36 @@ import numpy as np
 from gpu_util import unpack_k, unpack_v
 
 
+def operand_offset(r, col):
+    """The layout text: the 16-byte chunk holding columns 32g+16h..+16 of row r
+    (lane l = 16g + r%16 of the MFMA operand for row block r//16) is chunk
+    (2*(r//16) + h)*64 + l."""
+    c = col // 16
+    g, h = c // 2, c % 2
+    lane = 16 * g + r % 16
+    return ((2 * (r // 16) + h) * 64 + lane) * 16 + col % 16
+
+
 def pack_k(codes):
     S = codes.shape[0]
     nT = -(-S // 128)
-    out = np.zeros((nT, 128, 128), np.uint8)
+    out = np.zeros((nT, 16384), np.uint8)
     for j in range(S):
         t, r = divmod(j, 128)
         for ch in range(128):
-            c = ch // 16
-            out[t, r, 16 * (c ^ (r & 7)) + ch % 16] = codes[j, ch]
+            out[t, operand_offset(r, ch)] = codes[j, ch]
     return out.reshape(-1)
 
 
 def pack_v(codes):
     S = codes.shape[0]
     nT = -(-S // 128)
-    out = np.zeros((nT, 128, 128), np.uint8)
+    out = np.zeros((nT, 16384), np.uint8)
     for j in range(S):
         t, jj = divmod(j, 128)
         kk = 32 * ((jj >> 2) & 3) + 4 * (jj >> 4) + (jj & 3)
         for d in range(128):
-            out[t, d, 16 * ((kk >> 4) ^ (d & 7)) + (kk & 15)] = codes[j, d]
+            out[t, operand_offset(d, kk)] = codes[j, d]
     return out.reshape(-1)
 
 
