@@ -242,12 +242,13 @@ def attention_prepared(prep: Prepared, with_repair=None, out=None):
     return out
 
 
-def debug_pcodes(prep: Prepared, b: int, h: int):
-    """Bytes the attention kernel wrote for every (query, key) of one (b, h),
-    the running row max it used per key tile, and the output."""
+def debug_pcodes(prep: Prepared, b: int, h: int, with_codes: bool = True):
+    """Bytes the attention kernel wrote for every (query, key) of one (b, h)
+    (None when with_codes is False), the running row max it used per key
+    tile, and the output."""
     B, S, H, _ = prep.shape
     nT = prep.plan.layout.n_ktiles
-    codes = torch.zeros((S, S), dtype=torch.uint8, device=prep.device)
+    codes = torch.zeros((S, S), dtype=torch.uint8, device=prep.device) if with_codes else None
     m_used = torch.full((S, nT), -(1 << 30), dtype=torch.int32, device=prep.device)
     out = torch.zeros(prep.shape, dtype=torch.bfloat16, device=prep.device)
     _check(_lib.oc_attn_debug_pcodes(prep.plan.handle, _ptr(prep.ws), prep.ws.numel(), b, h, _ptr(codes),

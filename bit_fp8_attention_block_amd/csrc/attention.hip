@@ -226,13 +226,15 @@ __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], co
     for (int qb = 0; qb < QBW; ++qb) {
       const int qrow = qrow0 + 16 * qb;
       if (qrow < a.S) {
+        if (a.dump_codes != nullptr) {
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb)
+          for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = j * KTILE + 16 * kb + 4 * g + r;
-            if (key < a.S) a.dump_codes[(int64_t)qrow * a.S + key] = (uint8_t)((uint32_t)P[qb][kb] >> (8 * r));
-          }
+            for (int r = 0; r < 4; ++r) {
+              const int key = j * KTILE + 16 * kb + 4 * g + r;
+              if (key < a.S) a.dump_codes[(int64_t)qrow * a.S + key] = (uint8_t)((uint32_t)P[qb][kb] >> (8 * r));
+            }
+        }
         if (g == 0) a.dump_m[(int64_t)qrow * a.nT + j] = (int32_t)Mn[qb];
       }
     }

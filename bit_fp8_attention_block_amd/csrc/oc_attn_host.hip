@@ -392,9 +392,9 @@ oc_status oc_attn_forward_prepared(oc_attn_plan* p, const void* ws, size_t ws_by
 
 oc_status oc_attn_debug_pcodes(oc_attn_plan* p, const void* ws, size_t ws_bytes, int32_t b, int32_t h,
                                uint8_t* codes, int32_t* m_used, void* out, void* stream) {
-  if (!p || !ws || !codes || !m_used || !out) return OC_ERR_INVALID_ARGUMENT;
+  if (!p || !ws || !m_used || !out) return OC_ERR_INVALID_ARGUMENT;
   if (b < 0 || b >= p->d.B || h < 0 || h >= p->d.H) return OC_ERR_INVALID_ARGUMENT;
-  if (p->d.S > 8192) return OC_ERR_UNSUPPORTED;
+  if (codes && p->d.S > 8192) return OC_ERR_UNSUPPORTED;
   if (ws_bytes < p->L.total_bytes) return OC_ERR_WORKSPACE_TOO_SMALL;
   if (p->prepared_state(ws) == -2) return OC_ERR_NOT_PREPARED;
   AttnArgs a = attn_args(p, ws, out, 0);

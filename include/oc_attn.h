@@ -167,12 +167,13 @@ oc_status oc_attn_forward_v_repair(oc_attn_plan* plan, const void* q, const void
 oc_status oc_attn_forward_prepared(oc_attn_plan* plan, const void* ws, size_t ws_bytes, void* out,
                                    int with_repair, void* stream);
 
-/* Parity aid: run the attention kernel on the prepared workspace for the one
- * (b, h) pair and dump, for every query row < S, the ExpCast byte it wrote
- * for every key (codes: device u8 [S][S]) and the running row max it used for
- * each key tile (m_used: device i32 [S][n_ktiles], indexed by tile number).
- * out receives the normal output for that (b, h). Only for S <= 8192;
- * larger S gives OC_ERR_UNSUPPORTED. */
+/* Parity aid: run the attention kernel (without repair) on the prepared
+ * workspace for the one (b, h) pair and dump, for every query row < S, the
+ * running row max it used for each key tile (m_used: device i32
+ * [S][n_ktiles], indexed by tile number) and, if codes is not NULL, the
+ * ExpCast byte it wrote for every key (codes: device u8 [S][S]; only for
+ * S <= 8192, larger S gives OC_ERR_UNSUPPORTED). out receives the normal
+ * output for that (b, h). */
 oc_status oc_attn_debug_pcodes(oc_attn_plan* plan, const void* ws, size_t ws_bytes, int32_t b, int32_t h,
                                uint8_t* codes, int32_t* m_used, void* out, void* stream);
 

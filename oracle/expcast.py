@@ -257,7 +257,8 @@ def key_tile_order(n_tiles: int) -> list:
     return order
 
 
-def expcast_attention_online(q, k, v, tau=None, rows=None, budget=0.0, ph=None, order="mid", chunk=256):
+def expcast_attention_online(q, k, v, tau=None, rows=None, budget=0.0, ph=None, order="mid", chunk=256,
+                             m_trace=None):
     """Single-pass (flash) form of ExpCast attention, as the pages' kernel runs
     it: keys are consumed in 128-key tiles in `order` ("mid" = key_tile_order,
     "ascending" = 0, 1, 2, ...). Per row, a running bit-aligned max M is raised
@@ -269,6 +270,12 @@ def expcast_attention_online(q, k, v, tau=None, rows=None, budget=0.0, ph=None, 
     It equals expcast_attention_head except for keys whose byte relative to
     the final max would fall below the normal E4M3 range (the underflow tail):
     those are kept more precisely when they were visited before the max.
+
+    m_trace, if given, is an integer array [len(rows), n_tiles] holding, by
+    tile number, the running max to use for that tile's bytes instead of the
+    one computed here (to replay another implementation's max decisions,
+    which can differ where a tile's largest logit is within rounding of an
+    integer). The rescale factors then follow from consecutive entries.
     """
     S, D = k.shape
     tau = 1.0 / math.sqrt(D) if tau is None else tau
@@ -281,6 +288,7 @@ def expcast_attention_online(q, k, v, tau=None, rows=None, budget=0.0, ph=None, 
     out = np.empty((len(rows), D))
     Ms = np.empty(len(rows), dtype=np.int64)
     Ls = np.empty(len(rows))
+    trace = np.zeros((len(rows), nT), dtype=np.int64)
     for c0 in range(0, len(rows), chunk):
         r = rows[c0:c0 + chunk]
         x = log2_logits(ph, r, tau)
@@ -290,12 +298,16 @@ def expcast_attention_online(q, k, v, tau=None, rows=None, budget=0.0, ph=None, 
         for t in tiles:
             ks = slice(t * QK_BLOCK, min(S, (t + 1) * QK_BLOCK))
             xt = x[:, ks]
-            Mn = np.maximum(M, np.ceil(xt.max(axis=1)))
+            if m_trace is None:
+                Mn = np.maximum(M, np.ceil(xt.max(axis=1)))
+            else:
+                Mn = np.asarray(m_trace[c0:c0 + len(r), t], dtype=np.float64)
             f = np.where(np.isinf(M), 0.0, np.exp2(M - Mn))     # exact powers of two
             P = VALUES[expcast_codes(xt, Mn)]
             O = O * f[:, None] + P @ vd[ks]
             L = L * f + P.sum(axis=1)
             M = Mn
+            trace[c0:c0 + len(r), t] = Mn.astype(np.int64)
         O *= float(ph.sv)
         if ph.repair is not None and ph.repair.k > 0:
             rp = ph.repair
@@ -304,7 +316,7 @@ def expcast_attention_online(q, k, v, tau=None, rows=None, budget=0.0, ph=None, 
         out[c0:c0 + len(r)] = O / L[:, None]
         Ms[c0:c0 + len(r)] = M.astype(np.int64)
         Ls[c0:c0 + len(r)] = L
-    return {"out": out, "M": Ms, "L": Ls, "ph": ph}
+    return {"out": out, "M": Ms, "L": Ls, "ph": ph, "m_trace": trace}
 
 
 def exact_attention_head(q, k, v, tau=None, rows=None, chunk=512):

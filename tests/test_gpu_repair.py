@@ -60,10 +60,14 @@ def test_repaired_output_matches_oracle(name, budget, rows_per_head, pairs):
     log(f"[repair out] {name} budget={budget}")
     q, k, v = workloads.make_inputs(name, device="cuda")
     out = oc.attention_v_repair(q, k, v, budget)
+    prep = oc.prepare(q, k, v)
     torch.cuda.synchronize()
     rows = np.array(workloads.sample_rows(w.S, rows_per_head, seed=w.seed))
     for b, h in pairs:
-        r = oracle_rows(q, k, v, b, h, rows, budget=budget)
+        # replay the kernel's running-max decisions (see test_gpu_attention._compare)
+        _, m_used, _ = oc.debug_pcodes(prep, b, h, with_codes=False)
+        m_trace = m_used[torch.as_tensor(rows, device=m_used.device)].cpu().numpy()
+        r = oracle_rows(q, k, v, b, h, rows, budget=budget, m_trace=m_trace)
         got = out_rows(out, b, h, rows)
         e = oracle.rel_l2(got, r["out"])
         log(f"  ({b},{h}) rel-L2 {e:.2e}")

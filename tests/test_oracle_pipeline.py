@@ -268,3 +268,18 @@ def test_online_and_two_pass_differ_only_through_the_underflow_tail():
     bound = 2.0 * tail * vmax / b["L"]            # |dO| <= (tail mass difference) * max|v| / L, both forms
     dO = np.abs(a["out"] - b["out"]).max(axis=1)
     assert np.all(dO <= bound + 1e-12)
+
+
+def test_online_replays_a_max_trace():
+    """Feeding the single-pass form its own running-max sequence reproduces
+    it exactly; raising every entry by one only moves weights that sit in the
+    underflow tail (bytes shift by 8, normal values by exact factors of 2)."""
+    q, k, v = workloads.make_inputs("s8192_h8", S=1500, H=1)
+    qh, kh, vh = (t[0, :, 0].double().numpy() for t in (q, k, v))
+    rows = np.arange(0, 1500, 37)
+    a = oracle.expcast_attention_online(qh, kh, vh, rows=rows)
+    b = oracle.expcast_attention_online(qh, kh, vh, rows=rows, m_trace=a["m_trace"])
+    np.testing.assert_array_equal(a["out"], b["out"])
+    c = oracle.expcast_attention_online(qh, kh, vh, rows=rows, m_trace=a["m_trace"] + 1)
+    assert oracle.rel_l2(c["out"], a["out"]) < 0.05
+    np.testing.assert_array_equal(c["M"], a["M"] + 1)
