@@ -76,33 +76,50 @@ __device__ inline int tile_at(int s, int c, int nT, int order) {
 
 // One 16 KiB tile from global memory into LDS by direct global->LDS loads:
 // 1024 chunks of 16 bytes; each instruction moves 1 KiB per wave, lane l's
-// chunk landing at wave base + 16*l.
+// chunk landing at wave base + 16*l (the base is taken from M0).
+// Written as inline assembly so that the compiler does not track these loads:
+// it would otherwise drain all of them (vmcnt(0)) before every LDS read and
+// at every barrier, which rules out keeping a tile load in flight across an
+// iteration. The caller orders them with explicit vmcnt waits and
+// lds_barrier(). The s_nop covers the M0-write -> LDS-DMA hazard.
 template <int NT>
 __device__ inline void load_tile(uint8_t* lds_dst, const uint8_t* src) {
   const int tid = threadIdx.x, wv = tid >> 6;
 #pragma unroll
   for (int i = 0; i < 1024 / NT; ++i) {
     const int ci = i * NT + tid;
-    __builtin_amdgcn_global_load_lds(src + ci * 16,
-                                     (__attribute__((address_space(3))) void*)(lds_dst + (i * NT + wv * 64) * 16),
-                                     16, 0, 0);
+    const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(
+        lds_dst + (i * NT + wv * 64) * 16);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src + ci * 16)
+                 : "memory", "m0");
   }
+}
+
+// Workgroup barrier that orders LDS accesses only (a full __syncthreads
+// fence would also wait for every outstanding global load)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 __device__ inline float max_over_row_lanes(float m) {
   // the 4 lanes l, l^16, l^32, l^48 hold the same query
   const uint32_t u = __float_as_uint(m);
   auto s16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  m = __builtin_fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+  m = __builtin_elementwise_maximum(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
   const uint32_t u2 = __float_as_uint(m);
   auto s32 = __builtin_amdgcn_permlane32_swap(u2, u2, false, false);
-  return __builtin_fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
 }
 
 constexpr int QBW = 2;            // 16-query blocks per wave
 constexpr int NWAVES = 8;         // 2 waves per SIMD: one of each group
 constexpr int NTHREADS = 64 * NWAVES;
-constexpr int LDS_BYTES = 6 * TILE_BYTES;   // K and V, three buffers each
+constexpr int NBUF = 4;                    // K and V tiles, four buffers each
+constexpr int LDS_BYTES = 2 * NBUF * TILE_BYTES;
 
 // scheduling-group masks of __builtin_amdgcn_sched_group_barrier
 constexpr int SG_MFMA = 0x008, SG_VALU = 0x002, SG_DS_READ = 0x100;
@@ -155,16 +172,20 @@ __device__ __forceinline__ void pv_tile(const uint8_t* vt, const v8i (&P)[QBW], 
   __builtin_amdgcn_sched_group_barrier(SG_MFMA, 3 * QBW, 0);
 }
 
-// max of the 32 scores a lane holds for one 16-query block, as a tree of
-// v_max3 so the dependent chain is 4 deep instead of 16
+// NaN-propagating maximum: scores are finite or -inf, and unlike fmaxf this
+// needs no canonicalisation of MFMA results, so it maps to one v_maximum3_f32
+// per two new operands
+__device__ __forceinline__ float fmax_p(float x, float y) { return __builtin_elementwise_maximum(x, y); }
+
+// max of the 32 scores a lane holds for one 16-query block, as a tree whose
+// dependent chain is 4 deep
 __device__ __forceinline__ float lane_max32(const v4f (&Sc)[8]) {
   float t[8];
 #pragma unroll
-  for (int kb = 0; kb < 8; ++kb)
-    t[kb] = __builtin_fmaxf(__builtin_fmaxf(Sc[kb][0], Sc[kb][1]), __builtin_fmaxf(Sc[kb][2], Sc[kb][3]));
-  const float a = __builtin_fmaxf(__builtin_fmaxf(t[0], t[1]), t[2]);
-  const float b = __builtin_fmaxf(__builtin_fmaxf(t[3], t[4]), t[5]);
-  return __builtin_fmaxf(__builtin_fmaxf(a, b), __builtin_fmaxf(t[6], t[7]));
+  for (int kb = 0; kb < 8; ++kb) t[kb] = fmax_p(fmax_p(fmax_p(Sc[kb][0], Sc[kb][1]), Sc[kb][2]), Sc[kb][3]);
+  const float a = fmax_p(fmax_p(t[0], t[1]), t[2]);
+  const float b = fmax_p(fmax_p(t[3], t[4]), t[5]);
+  return fmax_p(fmax_p(a, b), fmax_p(t[6], t[7]));
 }
 
 // ExpCast for one tile and the wave's two 16-query blocks: raise the running
@@ -194,7 +215,7 @@ __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], co
   for (int qb = 0; qb < QBW; ++qb) {
     aqs[qb] = aq[qb] * skj;
     const float m = max_over_row_lanes(lane_max32(S[qb]));
-    Mn[qb] = __builtin_fmaxf(M[qb], __builtin_ceilf((aqs[qb] * m) * 0.125f));
+    Mn[qb] = fmax_p(M[qb], __builtin_ceilf((aqs[qb] * m) * 0.125f));
     grow |= Mn[qb] > M[qb];
   }
   if (__builtin_amdgcn_ballot_w64(grow) != 0) {
@@ -247,13 +268,15 @@ __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], co
 // issues MFMAs while the other runs the VALU part:
 //   group A, iteration s:  ExpCast(s) | PV(s), QK(s+1)
 //   group B, iteration s:  PV(s-1), QK(s) | ExpCast(s)
-// Iteration s reads K tiles s and s+1 and V tiles s-1 and s while K s+2 and
-// V s+1 stream in, so K and V are triple-buffered in LDS (96 KiB).
+// Iteration s reads K tiles s and s+1 and V tiles s-1 and s. The loads issued
+// in iteration s (K s+3, V s+2) may stay in flight until the end of
+// iteration s+1, which hides L2 misses; so K and V get four LDS buffers each
+// (128 KiB).
 template <bool REPAIR, bool DUMP>
 __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   uint8_t* const kbuf = smem;
-  uint8_t* const vbuf = smem + 3 * TILE_BYTES;
+  uint8_t* const vbuf = smem + NBUF * TILE_BYTES;
 
   int b, h, qt;
   if (DUMP) {
@@ -303,43 +326,54 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
 
   const uint8_t* kg = a.kpack + (int64_t)bh * nT * TILE_BYTES;
   const uint8_t* vg = a.vpack + (int64_t)bh * nT * TILE_BYTES;
-  const float* skp = a.sk + (int64_t)bh * nT;
+  // per-tile K scales through the scalar cache: a vector load here would sit
+  // behind the tile loads in the vector memory counter
+  const __attribute__((address_space(4))) float* skp =
+      (const __attribute__((address_space(4))) float*)(a.sk + (int64_t)bh * nT);
   const int centre = (nT - 1) >> 1;
   const int last_masked = (a.S & (KTILE - 1)) ? nT - 1 : -1;
 
-  load_tile<NTHREADS>(kbuf, kg + (int64_t)tile_at(0, centre, nT, a.order) * TILE_BYTES);
-  load_tile<NTHREADS>(vbuf, vg + (int64_t)tile_at(0, centre, nT, a.order) * TILE_BYTES);
-  if (nT > 1) load_tile<NTHREADS>(kbuf + TILE_BYTES, kg + (int64_t)tile_at(1, centre, nT, a.order) * TILE_BYTES);
+  const auto kt_ptr = [&](int step) { return kg + (int64_t)tile_at(step, centre, nT, a.order) * TILE_BYTES; };
+  const auto vt_ptr = [&](int step) { return vg + (int64_t)tile_at(step, centre, nT, a.order) * TILE_BYTES; };
+  // prologue: K tiles 0..2 and V tiles 0..1
+#pragma unroll
+  for (int i = 0; i < 3; ++i)
+    if (i < nT) load_tile<NTHREADS>(kbuf + i * TILE_BYTES, kt_ptr(i));
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    if (i < nT) load_tile<NTHREADS>(vbuf + i * TILE_BYTES, vt_ptr(i));
   __builtin_amdgcn_s_waitcnt(0);   // this wave's chunks are in LDS
   __syncthreads();
   if (!group_b) qk_tile(kbuf, qop, S, lane);
 
-  int ks = 0;   // buffer index of K tile s (= s % 3)
   for (int s = 0; s < nT; ++s) {
     const int j = tile_at(s, centre, nT, a.order);
-    const int ks1 = ks == 2 ? 0 : ks + 1, ks2 = ks1 == 2 ? 0 : ks1 + 1;   // s+1, s+2 (and s-1) mod 3
-    if (s + 2 < nT) load_tile<NTHREADS>(kbuf + ks2 * TILE_BYTES, kg + (int64_t)tile_at(s + 2, centre, nT, a.order) * TILE_BYTES);
-    if (s + 1 < nT) load_tile<NTHREADS>(vbuf + ks1 * TILE_BYTES, vg + (int64_t)tile_at(s + 1, centre, nT, a.order) * TILE_BYTES);
+    const int b0 = s & (NBUF - 1), b1 = (s + 1) & (NBUF - 1), bm1 = (s - 1) & (NBUF - 1);
+    const bool ld_k = s + 3 < nT, ld_v = s + 2 < nT;
+    if (ld_k) load_tile<NTHREADS>(kbuf + ((s + 3) & (NBUF - 1)) * TILE_BYTES, kt_ptr(s + 3));
+    if (ld_v) load_tile<NTHREADS>(vbuf + ((s + 2) & (NBUF - 1)) * TILE_BYTES, vt_ptr(s + 2));
     const float skj = skp[j];
     if (!group_b) {
       expcast_tile<DUMP>(S, P, aq, skj, M, O, L, j, j == last_masked, a, g, qrow0);
-      pv_tile(vbuf + ks * TILE_BYTES, P, O, L, lane);
-      if (s + 1 < nT) qk_tile(kbuf + ks1 * TILE_BYTES, qop, S, lane);
+      pv_tile(vbuf + b0 * TILE_BYTES, P, O, L, lane);
+      if (s + 1 < nT) qk_tile(kbuf + b1 * TILE_BYTES, qop, S, lane);
     } else {
       // QK first: its results are ready by the time the PV MFMAs have issued
-      qk_tile(kbuf + ks * TILE_BYTES, qop, S, lane);
-      if (s > 0) pv_tile(vbuf + ks2 * TILE_BYTES, P, O, L, lane);   // V tile s-1 sits in buffer (s+2) % 3
+      qk_tile(kbuf + b0 * TILE_BYTES, qop, S, lane);
+      if (s > 0) pv_tile(vbuf + bm1 * TILE_BYTES, P, O, L, lane);
       expcast_tile<DUMP>(S, P, aq, skj, M, O, L, j, j == last_masked, a, g, qrow0);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    ks = ks1;
+    // wait for the loads issued one iteration ago (each tile is 2 per thread);
+    // this iteration's stay in flight
+    // (the code dump's stores also count, so that path drains everything)
+    if (DUMP) __builtin_amdgcn_s_waitcnt(0x0F70);                           // vmcnt(0)
+    else if (ld_k && ld_v) __builtin_amdgcn_s_waitcnt(0x0F74);              // vmcnt(4)
+    else if (ld_k || ld_v) __builtin_amdgcn_s_waitcnt(0x0F72);              // vmcnt(2)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+    lds_barrier();
   }
-  if (group_b) {
-    // V tile nT-1 is in buffer (nT-1) % 3 = (ks + 2) % 3 after the loop
-    const int kl = ks == 0 ? 2 : ks - 1;
-    pv_tile(vbuf + kl * TILE_BYTES, P, O, L, lane);
-  }
+  if (group_b) pv_tile(vbuf + ((nT - 1) & (NBUF - 1)) * TILE_BYTES, P, O, L, lane);
+  __builtin_amdgcn_s_waitcnt(0);
 
   float scale = a.sv[2 * bh];
   if (REPAIR && a.n_sel > 0) {
@@ -425,9 +459,9 @@ static hipError_t launch_one(const AttnArgs& a, dim3 grid, hipStream_t st) {
 }
 
 hipError_t launch_attention(const AttnArgs& a, bool repair, bool dump, hipStream_t st) {
-  if (dump) return launch_one<false, true>(a, dim3(a.nQT), st);
   const int nwork = a.B * a.H * a.nQT;
-  const dim3 grid(8 * ((nwork + 7) / 8));
+  const dim3 grid = dump ? dim3(a.nQT) : dim3(8 * ((nwork + 7) / 8));
+  if (dump) return launch_one<false, true>(a, grid, st);
   return repair ? launch_one<true, false>(a, grid, st) : launch_one<false, false>(a, grid, st);
 }
 
