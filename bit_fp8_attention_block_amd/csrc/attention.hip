@@ -177,15 +177,23 @@ __device__ __forceinline__ void pv_tile(const uint8_t* vt, const v8i (&P)[QBW], 
 // per two new operands
 __device__ __forceinline__ float fmax_p(float x, float y) { return __builtin_elementwise_maximum(x, y); }
 
-// max of the 32 scores a lane holds for one 16-query block, as a tree whose
-// dependent chain is 4 deep
+// max of the 32 scores a lane holds for one 16-query block: two chains of
+// three-operand maxima (17 instructions, dependent depth 9)
 __device__ __forceinline__ float lane_max32(const v4f (&Sc)[8]) {
-  float t[8];
+  float c[2];
 #pragma unroll
-  for (int kb = 0; kb < 8; ++kb) t[kb] = fmax_p(fmax_p(fmax_p(Sc[kb][0], Sc[kb][1]), Sc[kb][2]), Sc[kb][3]);
-  const float a = fmax_p(fmax_p(t[0], t[1]), t[2]);
-  const float b = fmax_p(fmax_p(t[3], t[4]), t[5]);
-  return fmax_p(fmax_p(a, b), fmax_p(t[6], t[7]));
+  for (int h = 0; h < 2; ++h) {
+    const v4f* x = Sc + 4 * h;
+    float m = fmax_p(fmax_p(x[0][0], x[0][1]), x[0][2]);
+    m = fmax_p(fmax_p(m, x[0][3]), x[1][0]);
+    m = fmax_p(fmax_p(m, x[1][1]), x[1][2]);
+    m = fmax_p(fmax_p(m, x[1][3]), x[2][0]);
+    m = fmax_p(fmax_p(m, x[2][1]), x[2][2]);
+    m = fmax_p(fmax_p(m, x[2][3]), x[3][0]);
+    m = fmax_p(fmax_p(m, x[3][1]), x[3][2]);
+    c[h] = fmax_p(m, x[3][3]);
+  }
+  return fmax_p(c[0], c[1]);
 }
 
 // ExpCast for one tile and the wave's two 16-query blocks: raise the running
@@ -266,8 +274,12 @@ __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], co
 // 0-3 (group A) and 4-7 (group B) share the SIMDs pairwise and run the
 // same tile loop half an iteration apart, so that on every SIMD one wave
 // issues MFMAs while the other runs the VALU part:
-//   group A, iteration s:  ExpCast(s) | PV(s), QK(s+1)
-//   group B, iteration s:  PV(s-1), QK(s) | ExpCast(s)
+//   group A, iteration s:  loads, ExpCast(s) | PV(s), QK(s+1)
+//   group B, iteration s:  QK(s), PV(s-1)    | ExpCast(s)
+// Group B starts its MFMAs right after the barrier, at raised priority, so
+// the partner wave's MFMAs do not interleave with them and delay B's ExpCast.
+// Only group A issues the tile loads (issuing the 32 KiB of one iteration
+// takes several hundred cycles, which would otherwise hold back B's MFMAs).
 // Iteration s reads K tiles s and s+1 and V tiles s-1 and s. The loads issued
 // in iteration s (K s+3, V s+2) may stay in flight until the end of
 // iteration s+1, which hides L2 misses; so K and V get four LDS buffers each
@@ -350,25 +362,26 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
     const int j = tile_at(s, centre, nT, a.order);
     const int b0 = s & (NBUF - 1), b1 = (s + 1) & (NBUF - 1), bm1 = (s - 1) & (NBUF - 1);
     const bool ld_k = s + 3 < nT, ld_v = s + 2 < nT;
-    if (ld_k) load_tile<NTHREADS>(kbuf + ((s + 3) & (NBUF - 1)) * TILE_BYTES, kt_ptr(s + 3));
-    if (ld_v) load_tile<NTHREADS>(vbuf + ((s + 2) & (NBUF - 1)) * TILE_BYTES, vt_ptr(s + 2));
+    if (ld_k && !group_b) load_tile<NTHREADS / 2>(kbuf + ((s + 3) & (NBUF - 1)) * TILE_BYTES, kt_ptr(s + 3));
+    if (ld_v && !group_b) load_tile<NTHREADS / 2>(vbuf + ((s + 2) & (NBUF - 1)) * TILE_BYTES, vt_ptr(s + 2));
     const float skj = skp[j];
     if (!group_b) {
       expcast_tile<DUMP>(S, P, aq, skj, M, O, L, j, j == last_masked, a, g, qrow0);
       pv_tile(vbuf + b0 * TILE_BYTES, P, O, L, lane);
       if (s + 1 < nT) qk_tile(kbuf + b1 * TILE_BYTES, qop, S, lane);
     } else {
-      // QK first: its results are ready by the time the PV MFMAs have issued
+      __builtin_amdgcn_s_setprio(2);
       qk_tile(kbuf + b0 * TILE_BYTES, qop, S, lane);
       if (s > 0) pv_tile(vbuf + bm1 * TILE_BYTES, P, O, L, lane);
+      __builtin_amdgcn_s_setprio(0);
       expcast_tile<DUMP>(S, P, aq, skj, M, O, L, j, j == last_masked, a, g, qrow0);
     }
-    // wait for the loads issued one iteration ago (each tile is 2 per thread);
-    // this iteration's stay in flight
-    // (the code dump's stores also count, so that path drains everything)
-    if (DUMP) __builtin_amdgcn_s_waitcnt(0x0F70);                           // vmcnt(0)
-    else if (ld_k && ld_v) __builtin_amdgcn_s_waitcnt(0x0F74);              // vmcnt(4)
-    else if (ld_k || ld_v) __builtin_amdgcn_s_waitcnt(0x0F72);              // vmcnt(2)
+    // group A waits for the loads it issued one iteration ago (a tile is 4
+    // loads per thread); this iteration's stay in flight. The code dump's
+    // stores also count, so that path drains everything.
+    if (DUMP || group_b) __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0)
+    else if (ld_k && ld_v) __builtin_amdgcn_s_waitcnt(0x0F78);              // vmcnt(8)
+    else if (ld_k || ld_v) __builtin_amdgcn_s_waitcnt(0x0F74);              // vmcnt(4)
     else __builtin_amdgcn_s_waitcnt(0x0F70);
     lds_barrier();
   }

@@ -48,7 +48,6 @@ struct oc_attn_plan {
   oc_attn_ws_layout L;
   int order;
   int grouping;
-  int variant;
   // cached prepare graph
   hipGraphExec_t gexec = nullptr;
   hipStream_t cap_stream = nullptr;
@@ -223,7 +222,6 @@ static AttnArgs attn_args(const oc_attn_plan* p, const void* ws, void* out, int 
   a.c8 = (float)(8.0 * (double)p->tau * 1.4426950408889634);
   a.order = p->order;
   a.grouping = p->grouping;
-  a.variant = p->variant;
   return a;
 }
 
@@ -309,8 +307,6 @@ oc_status oc_attn_plan_create(const oc_attn_desc* desc, double max_repair_budget
   p->order = (order && std::atoi(order) == 1) ? 1 : 0;
   const char* grouping = std::getenv("OC_ATTN_GROUPING");
   p->grouping = (grouping && std::atoi(grouping) == 1) ? 1 : 0;
-  const char* variant = std::getenv("OC_ATTN_VARIANT");
-  p->variant = variant ? std::atoi(variant) : 0;
   compute_layout(p);
   *plan = p;
   return OC_OK;
