@@ -12,8 +12,10 @@ is one JSON record:
                stream the kernel is launched on, over --steps kernel-only calls
   cpu_baseline the CPU oracle (float64 numpy) timed on a bounded sample of the
                same workload on this host's cores
-plus the prepare time, the repaired call, and a BF16 attention run through
-torch's SDPA on the same GPU for comparison. Progress goes to stderr.
+plus the prepare time, the repaired call, the same attention kernel on the
+byte path ExpCast replaces (one exponential per score, then the FP32->FP8
+cast), and a BF16 attention run through torch's SDPA on the same GPU for
+comparison. Progress goes to stderr.
 """
 from __future__ import annotations
 
@@ -160,6 +162,10 @@ def main():
         print(json.dumps({"kernel_ms": k_ms, "kernel_tflops": flop / k_ms / 1e9}))
         return
     kr_ms, _ = timed_calls(lambda: oc.attention_prepared(prep, with_repair=True, out=out), args.steps, 1)
+    # the same kernel on the byte path ExpCast replaces (exponential + FP8 cast)
+    log("[bench] attention kernel alone, exponential + FP8-cast weights")
+    ke_ms, _ = timed_calls(lambda: oc.attention_prepared(prep, with_repair=False, out=out, weights="exp_fp8"),
+                           args.steps, 1)
     del prep
 
     # full call (prepare graph + attention), the headline step
@@ -221,6 +227,8 @@ def main():
         "kernel_ms": round(k_ms, 4),
         "kernel_tflops": round(kernel_tflops, 2),
         "kernel_repair_ms": round(kr_ms, 4),
+        "kernel_exp_fp8_ms": round(ke_ms, 4),
+        "expcast_speedup_vs_exp_fp8": round(ke_ms / k_ms, 3),
         "full_call_ms_events": round(full_ev_ms, 4),
         "prepare_ms": round(p_ms, 4),
         "prepare_gbs": round(prep_bytes / p_ms / 1e6, 1),

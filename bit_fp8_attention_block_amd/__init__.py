@@ -9,6 +9,7 @@ fallback path: if the library is missing, importing the binding raises.
     prep = prepare_v_repair(q, k, v, 0.005)      # quantize + pick repair tokens
     out = attention_v_repair(q, k, v, 0.005)     # full call with V-residual repair
     out = attention_prepared(prep, with_repair=True)   # attention on a prepared workspace
+    out = attention_prepared(prep, weights="exp_fp8")  # comparison path: exp + FP8 cast
 
 q, k, v: CUDA (HIP) tensors [B,S,H,128] or [S,H,128] in bf16 or fp16, with a
 contiguous channel dimension and 16-byte aligned rows. The output is bf16
@@ -26,6 +27,8 @@ LIB_PATH = os.path.join(_HERE, "liboc_attn.so")
 
 OC_OK, OC_ERR_INVALID_ARGUMENT, OC_ERR_UNSUPPORTED, OC_ERR_WORKSPACE_TOO_SMALL, OC_ERR_NOT_PREPARED, OC_ERR_HIP = range(6)
 OC_BF16, OC_FP16 = 0, 1
+# softmax-weight paths (oc_weights): ExpCast bytes, or exponential + FP32->E4M3 cast
+WEIGHTS = {"expcast": 0, "exp_fp8": 1}
 
 
 class OcAttnError(RuntimeError):
@@ -48,18 +51,20 @@ class WsLayout(ctypes.Structure):
 
 EXPORTS = ("oc_attn_plan_create", "oc_attn_plan_destroy", "oc_attn_workspace_size", "oc_attn_workspace_layout",
            "oc_attn_prepare", "oc_attn_forward", "oc_attn_prepare_v_repair", "oc_attn_forward_v_repair",
-           "oc_attn_forward_prepared", "oc_attn_debug_pcodes", "oc_attn_status_string", "oc_attn_last_hip_error")
+           "oc_attn_forward_prepared", "oc_attn_debug_pcodes", "oc_attn_status_string", "oc_attn_last_hip_error",
+           "oc_attn_plan_set_weights")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
-        raise ImportError(f"{path} is not built; run `python -m bit_fp8_attention_block_amd.build`")
+        raise ImportError(f"{path} is not built; run `python bit_fp8_attention_block_amd/build.py`")
     lib = ctypes.CDLL(path)
     P, VP, SZ, I32, I64, D = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
     st = ctypes.c_int
     lib.oc_attn_plan_create.argtypes = [ctypes.POINTER(Desc), D, ctypes.POINTER(P)]
     lib.oc_attn_plan_destroy.argtypes = [P]
     lib.oc_attn_plan_destroy.restype = None
+    lib.oc_attn_plan_set_weights.argtypes = [P, ctypes.c_int]
     lib.oc_attn_workspace_size.argtypes = [P, ctypes.POINTER(SZ)]
     lib.oc_attn_workspace_layout.argtypes = [P, ctypes.POINTER(WsLayout)]
     lib.oc_attn_prepare.argtypes = [P, VP, VP, VP, VP, SZ, VP]
@@ -71,7 +76,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.oc_attn_status_string.argtypes = [st]
     lib.oc_attn_status_string.restype = ctypes.c_char_p
     lib.oc_attn_last_hip_error.argtypes = []
-    for name in ("oc_attn_plan_create", "oc_attn_workspace_size", "oc_attn_workspace_layout", "oc_attn_prepare",
+    for name in ("oc_attn_plan_create", "oc_attn_plan_set_weights", "oc_attn_workspace_size", "oc_attn_workspace_layout", "oc_attn_prepare",
                  "oc_attn_forward", "oc_attn_prepare_v_repair", "oc_attn_forward_v_repair",
                  "oc_attn_forward_prepared", "oc_attn_debug_pcodes"):
         getattr(lib, name).restype = st
@@ -88,6 +93,12 @@ def _check(status, what):
         if status == OC_ERR_HIP:
             msg += f" (hipError_t {_lib.oc_attn_last_hip_error()})"
         raise OcAttnError(status, f"{what}: {msg}")
+
+
+def _set_weights(plan, weights):
+    if weights not in WEIGHTS:
+        raise OcAttnError(OC_ERR_INVALID_ARGUMENT, f"weights must be one of {sorted(WEIGHTS)}")
+    _check(_lib.oc_attn_plan_set_weights(plan.handle, WEIGHTS[weights]), "oc_attn_plan_set_weights")
 
 
 def _ptr(t):
@@ -206,10 +217,12 @@ def prepare_v_repair(q, k, v, budget, softmax_scale=None) -> Prepared:
     return prepare(q, k, v, budget, softmax_scale)
 
 
-def attention(q, k, v, softmax_scale=None, out=None):
-    """Full call: FP8 quantization + ExpCast attention, BF16 output."""
+def attention(q, k, v, softmax_scale=None, out=None, weights="expcast"):
+    """Full call: FP8 quantization + ExpCast attention, BF16 output.
+    weights="exp_fp8" runs the comparison path (exponential + FP8 cast)."""
     q, k, v, squeeze = _canon(q, k, v)
     plan = get_plan(q, softmax_scale, 0.0)
+    _set_weights(plan, weights)
     ws = _workspace(plan, q.device)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
@@ -218,11 +231,12 @@ def attention(q, k, v, softmax_scale=None, out=None):
     return out.squeeze(0) if squeeze else out
 
 
-def attention_v_repair(q, k, v, budget, softmax_scale=None, out=None):
+def attention_v_repair(q, k, v, budget, softmax_scale=None, out=None, weights="expcast"):
     """Full call with V-residual repair of the ceil(budget*S) worst-rounded
     value tokens of every (b, h)."""
     q, k, v, squeeze = _canon(q, k, v)
     plan = get_plan(q, softmax_scale, budget)
+    _set_weights(plan, weights)
     ws = _workspace(plan, q.device)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
@@ -231,8 +245,9 @@ def attention_v_repair(q, k, v, budget, softmax_scale=None, out=None):
     return out.squeeze(0) if squeeze else out
 
 
-def attention_prepared(prep: Prepared, with_repair=None, out=None):
+def attention_prepared(prep: Prepared, with_repair=None, out=None, weights="expcast"):
     """Attention only, on a workspace filled by prepare / prepare_v_repair."""
+    _set_weights(prep.plan, weights)
     if with_repair is None:
         with_repair = prep.budget is not None
     if out is None:
@@ -242,10 +257,11 @@ def attention_prepared(prep: Prepared, with_repair=None, out=None):
     return out
 
 
-def debug_pcodes(prep: Prepared, b: int, h: int, with_codes: bool = True):
+def debug_pcodes(prep: Prepared, b: int, h: int, with_codes: bool = True, weights="expcast"):
     """Bytes the attention kernel wrote for every (query, key) of one (b, h)
     (None when with_codes is False), the running row max it used per key
     tile, and the output."""
+    _set_weights(prep.plan, weights)
     B, S, H, _ = prep.shape
     nT = prep.plan.layout.n_ktiles
     codes = torch.zeros((S, S), dtype=torch.uint8, device=prep.device) if with_codes else None
@@ -262,4 +278,4 @@ def flops(B, S, H, D=128):
 
 
 __all__ = ["attention", "attention_v_repair", "prepare", "prepare_v_repair", "attention_prepared", "debug_pcodes",
-           "Plan", "Prepared", "OcAttnError", "flops", "load_library", "EXPORTS", "LIB_PATH"]
+           "Plan", "Prepared", "OcAttnError", "flops", "load_library", "EXPORTS", "LIB_PATH", "WEIGHTS"]

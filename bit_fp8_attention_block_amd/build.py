@@ -1,6 +1,9 @@
 """Build liboc_attn.so (gfx950) in-tree with hipcc.
 
-    python -m bit_fp8_attention_block_amd.build
+    python bit_fp8_attention_block_amd/build.py
+
+(run as a file, not through the package, whose import loads the library
+this builds)
 
 Every HIP translation unit is compiled for gfx950 only, with packed-FP32
 instructions disabled and floating-point contraction off (the kernels write

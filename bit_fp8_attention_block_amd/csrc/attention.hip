@@ -10,6 +10,11 @@
 // clamps). The byte never exceeds 120 because M >= ceil(a*s_raw/8), and
 // scores more than ~15 binades below the max land on 0.
 //
+// For comparison the same kernel can instead take the path ExpCast replaces
+// (weights selection OC_WEIGHTS_EXP_FP8): weight 256*2^(x - M) from v_exp_f32,
+// then the hardware FP32 -> E4M3 cast (v_cvt_pk_fp8_f32), with everything else
+// (max, rescale, sums, MFMAs) unchanged.
+//
 // Because M is an integer, the weights of earlier tiles relative to a stale M
 // differ from those relative to the new M by an exact power of two. The
 // rescale is then an exact v_ldexp on O and L, and the result does not depend
@@ -196,12 +201,35 @@ __device__ __forceinline__ float lane_max32(const v4f (&Sc)[8]) {
   return fmax_p(c[0], c[1]);
 }
 
+// Four scores of one query -> four E4M3 bytes (low byte first).
+// ExpCast: byte = clamp(rne(a*s + b), 0, 255), with a = 8*tau*log2(e)*sq*sk and
+// b = 119.65 - 8*M.
+__device__ __forceinline__ uint32_t bytes_expcast(const v4f& sc, float a, float b) {
+  uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sc[0], a, b), 0, 0u);
+  w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sc[1], a, b), 1, w);
+  w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sc[2], a, b), 2, w);
+  return __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sc[3], a, b), 3, w);
+}
+// Exp path: weight 2^(a8*s + b8) with a8 = a/8 and b8 = 8 - M, i.e. 256*2^(x - M)
+// (at most 256, so the cast never saturates; -inf gives 0), cast to E4M3 with
+// round-to-nearest-even by the hardware.
+__device__ __forceinline__ uint32_t bytes_exp_fp8(float e0, float e1, float e2, float e3) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false) & 0xFFFFu;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, (int)lo, true);
+}
+__device__ __forceinline__ uint32_t bytes_exp(const v4f& sc, float a8, float b8) {
+  return bytes_exp_fp8(__builtin_amdgcn_exp2f(__builtin_fmaf(sc[0], a8, b8)),
+                       __builtin_amdgcn_exp2f(__builtin_fmaf(sc[1], a8, b8)),
+                       __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2], a8, b8)),
+                       __builtin_amdgcn_exp2f(__builtin_fmaf(sc[3], a8, b8)));
+}
+
 // ExpCast for one tile and the wave's two 16-query blocks: raise the running
 // bit-aligned max (rescaling O and L by the exact power of two when it
 // grows), then one FMA and one saturating convert per score give the E4M3
 // bytes. Both blocks are handled side by side to give the VALU independent
 // work, with one (rarely taken) rescale branch.
-template <bool DUMP>
+template <bool DUMP, bool EXPP>
 __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], const float (&aq)[QBW], float skj,
                                              float (&M)[QBW], v4f (&O)[QBW][8], v4f (&L)[QBW], int j, bool masked,
                                              const AttnArgs& a, int g, int qrow0) {
@@ -243,12 +271,10 @@ __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], co
   for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
     for (int qb = 0; qb < QBW; ++qb) {
-      const float bq = __builtin_fmaf(-8.0f, Mn[qb], EXPCAST_C);
-      uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(S[qb][kb][0], aqs[qb], bq), 0, 0u);
-      w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(S[qb][kb][1], aqs[qb], bq), 1, w);
-      w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(S[qb][kb][2], aqs[qb], bq), 2, w);
-      w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(S[qb][kb][3], aqs[qb], bq), 3, w);
-      P[qb][kb] = (int)w;
+      if (EXPP)
+        P[qb][kb] = (int)bytes_exp(S[qb][kb], aqs[qb] * 0.125f, 8.0f - Mn[qb]);
+      else
+        P[qb][kb] = (int)bytes_expcast(S[qb][kb], aqs[qb], __builtin_fmaf(-8.0f, Mn[qb], EXPCAST_C));
     }
   if (DUMP) {
 #pragma unroll
@@ -284,7 +310,7 @@ __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], co
 // in iteration s (K s+3, V s+2) may stay in flight until the end of
 // iteration s+1, which hides L2 misses; so K and V get four LDS buffers each
 // (128 KiB).
-template <bool REPAIR, bool DUMP>
+template <bool REPAIR, bool DUMP, bool EXPP>
 __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   uint8_t* const kbuf = smem;
@@ -366,7 +392,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
     if (ld_v && !group_b) load_tile<NTHREADS / 2>(vbuf + ((s + 2) & (NBUF - 1)) * TILE_BYTES, vt_ptr(s + 2));
     const float skj = skp[j];
     if (!group_b) {
-      expcast_tile<DUMP>(S, P, aq, skj, M, O, L, j, j == last_masked, a, g, qrow0);
+      expcast_tile<DUMP, EXPP>(S, P, aq, skj, M, O, L, j, j == last_masked, a, g, qrow0);
       pv_tile(vbuf + b0 * TILE_BYTES, P, O, L, lane);
       if (s + 1 < nT) qk_tile(kbuf + b1 * TILE_BYTES, qop, S, lane);
     } else {
@@ -374,7 +400,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
       qk_tile(kbuf + b0 * TILE_BYTES, qop, S, lane);
       if (s > 0) pv_tile(vbuf + bm1 * TILE_BYTES, P, O, L, lane);
       __builtin_amdgcn_s_setprio(0);
-      expcast_tile<DUMP>(S, P, aq, skj, M, O, L, j, j == last_masked, a, g, qrow0);
+      expcast_tile<DUMP, EXPP>(S, P, aq, skj, M, O, L, j, j == last_masked, a, g, qrow0);
     }
     // group A waits for the loads it issued one iteration ago (a tile is 4
     // loads per thread); this iteration's stay in flight. The code dump's
@@ -423,12 +449,21 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int qb = 0; qb < QBW; ++qb) {
           const v4f sc = mfma_f8(kop, qop[qb], v4f{0.f, 0.f, 0.f, 0.f});
-          const float bq = __builtin_fmaf(-8.0f, M[qb], EXPCAST_C);
           uint32_t w = 0;
+          if (EXPP) {
+            float e[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float y = live[r] ? __builtin_fmaf(sc[r], aq[qb] * skk[r], bq) : -1.0f;
-            w = __builtin_amdgcn_cvt_pk_u8_f32(y, r, w);
+            for (int r = 0; r < 4; ++r)
+              e[r] = live[r] ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], aq[qb] * skk[r] * 0.125f, 8.0f - M[qb]))
+                             : 0.0f;
+            w = bytes_exp_fp8(e[0], e[1], e[2], e[3]);
+          } else {
+            const float bq = __builtin_fmaf(-8.0f, M[qb], EXPCAST_C);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float y = live[r] ? __builtin_fmaf(sc[r], aq[qb] * skk[r], bq) : -1.0f;
+              w = __builtin_amdgcn_cvt_pk_u8_f32(y, r, w);
+            }
           }
           P[qb][kb] = (int)w;
         }
@@ -458,24 +493,29 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   }
 }
 
-template <bool REPAIR, bool DUMP>
+template <bool REPAIR, bool DUMP, bool EXPP>
 static hipError_t launch_one(const AttnArgs& a, dim3 grid, hipStream_t st) {
   static bool configured = false;
   if (!configured) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<REPAIR, DUMP>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<REPAIR, DUMP, EXPP>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (e != hipSuccess) return e;
     configured = true;
   }
-  hipLaunchKernelGGL((attn_kernel<REPAIR, DUMP>), grid, dim3(NTHREADS), LDS_BYTES, st, a);
+  hipLaunchKernelGGL((attn_kernel<REPAIR, DUMP, EXPP>), grid, dim3(NTHREADS), LDS_BYTES, st, a);
   return hipGetLastError();
+}
+
+template <bool EXPP>
+static hipError_t launch_weights(const AttnArgs& a, bool repair, bool dump, dim3 grid, hipStream_t st) {
+  if (dump) return launch_one<false, true, EXPP>(a, grid, st);
+  return repair ? launch_one<true, false, EXPP>(a, grid, st) : launch_one<false, false, EXPP>(a, grid, st);
 }
 
 hipError_t launch_attention(const AttnArgs& a, bool repair, bool dump, hipStream_t st) {
   const int nwork = a.B * a.H * a.nQT;
   const dim3 grid = dump ? dim3(a.nQT) : dim3(8 * ((nwork + 7) / 8));
-  if (dump) return launch_one<false, true>(a, grid, st);
-  return repair ? launch_one<true, false>(a, grid, st) : launch_one<false, false>(a, grid, st);
+  return a.exp_path ? launch_weights<true>(a, repair, dump, grid, st) : launch_weights<false>(a, repair, dump, grid, st);
 }
 
 }  // namespace oc

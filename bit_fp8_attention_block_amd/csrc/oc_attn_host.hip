@@ -48,6 +48,7 @@ struct oc_attn_plan {
   oc_attn_ws_layout L;
   int order;
   int grouping;
+  int exp_path;          // oc_weights: 0 ExpCast, 1 exp + FP8 cast
   // cached prepare graph
   hipGraphExec_t gexec = nullptr;
   hipStream_t cap_stream = nullptr;
@@ -222,6 +223,7 @@ static AttnArgs attn_args(const oc_attn_plan* p, const void* ws, void* out, int 
   a.c8 = (float)(8.0 * (double)p->tau * 1.4426950408889634);
   a.order = p->order;
   a.grouping = p->grouping;
+  a.exp_path = p->exp_path;
   return a;
 }
 
@@ -309,6 +311,12 @@ oc_status oc_attn_plan_create(const oc_attn_desc* desc, double max_repair_budget
   p->grouping = (grouping && std::atoi(grouping) == 1) ? 1 : 0;
   compute_layout(p);
   *plan = p;
+  return OC_OK;
+}
+
+oc_status oc_attn_plan_set_weights(oc_attn_plan* p, int weights) {
+  if (!p || (weights != OC_WEIGHTS_EXPCAST && weights != OC_WEIGHTS_EXP_FP8)) return OC_ERR_INVALID_ARGUMENT;
+  p->exp_path = weights == OC_WEIGHTS_EXP_FP8 ? 1 : 0;
   return OC_OK;
 }
 

@@ -134,6 +134,22 @@ typedef struct oc_attn_plan oc_attn_plan;
 oc_status oc_attn_plan_create(const oc_attn_desc* desc, double max_repair_budget, oc_attn_plan** plan);
 /* Release a plan (and its cached graph). NULL is ignored. */
 void oc_attn_plan_destroy(oc_attn_plan* plan);
+/* Softmax-weight path of the attention kernel, for later oc_attn_forward*,
+ * oc_attn_forward_prepared and oc_attn_debug_pcodes calls on this plan
+ * (host-only; default OC_WEIGHTS_EXPCAST).
+ *   OC_WEIGHTS_EXPCAST: E4M3 bytes from one FMA on the log-domain score
+ *     (VC-Attention write-up, section "ExpCast-FP8").
+ *   OC_WEIGHTS_EXP_FP8: the path ExpCast replaces, kept to measure what it
+ *     saves (Open-VC news, section "Проблема: узкое место MUFU в FP8": one
+ *     exponential per score; VC-Attention write-up, section "ExpCast-FP8":
+ *     exponential, then an FP32->FP8 cast). Weight 256*2^(x - M) from one
+ *     v_exp_f32 per score (within 1 ulp of the rounded value), then the
+ *     hardware FP32->E4M3 cast, round-to-nearest-even. The running max,
+ *     rescales, row sums, MFMAs and repair are unchanged.
+ * Any other value gives OC_ERR_INVALID_ARGUMENT and leaves the plan as it
+ * was. */
+typedef enum oc_weights { OC_WEIGHTS_EXPCAST = 0, OC_WEIGHTS_EXP_FP8 = 1 } oc_weights;
+oc_status oc_attn_plan_set_weights(oc_attn_plan* plan, int weights);
 /* Workspace bytes the plan needs (host-only). */
 oc_status oc_attn_workspace_size(const oc_attn_plan* plan, size_t* bytes);
 /* Buffer offsets inside the workspace (host-only). */

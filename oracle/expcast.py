@@ -200,8 +200,10 @@ def expcast_attention_head(q, k, v, tau=None, rows=None, budget=0.0, ph=None,
     `out`, the row maxima `M`, row sums `L` and the prepared head `ph`.
 
     quantize=False skips the FP8 codec (unit scales, raw values);
-    weights="exp" uses the exact weights 2^(x - M) instead of ExpCast bytes.
-    With both switched off the result is textbook softmax attention.
+    weights="exp" uses the exact weights 2^(x - M) instead of ExpCast bytes,
+    and weights="exp_cast" the E4M3 cast of the fp32 weight 256*2^(x - M)
+    (the path ExpCast replaces, exp_cast_codes). With the codec and the
+    weights both switched off the result is textbook softmax attention.
     """
     S, D = k.shape
     tau = 1.0 / math.sqrt(D) if tau is None else tau
@@ -226,6 +228,8 @@ def expcast_attention_head(q, k, v, tau=None, rows=None, budget=0.0, ph=None,
         M = bitaligned_row_max(x)
         if weights == "expcast":
             P = VALUES[expcast_codes(x, M)]
+        elif weights == "exp_cast":
+            P = VALUES[exp_cast_codes(x, M)]
         elif weights == "exp":
             P = np.exp2(x - M[:, None])
         else:
@@ -258,7 +262,7 @@ def key_tile_order(n_tiles: int) -> list:
 
 
 def expcast_attention_online(q, k, v, tau=None, rows=None, budget=0.0, ph=None, order="mid", chunk=256,
-                             m_trace=None):
+                             m_trace=None, weights="expcast"):
     """Single-pass (flash) form of ExpCast attention, as the pages' kernel runs
     it: keys are consumed in 128-key tiles in `order` ("mid" = key_tile_order,
     "ascending" = 0, 1, 2, ...). Per row, a running bit-aligned max M is raised
@@ -276,7 +280,14 @@ def expcast_attention_online(q, k, v, tau=None, rows=None, budget=0.0, ph=None, 
     one computed here (to replay another implementation's max decisions,
     which can differ where a tile's largest logit is within rounding of an
     integer). The rescale factors then follow from consecutive entries.
+
+    weights="exp_cast" writes each tile's bytes by the path ExpCast replaces
+    (exp_cast_codes against the same running max) instead; everything else
+    is the same.
     """
+    if weights not in ("expcast", "exp_cast"):
+        raise ValueError(weights)
+    codes_of = expcast_codes if weights == "expcast" else exp_cast_codes
     S, D = k.shape
     tau = 1.0 / math.sqrt(D) if tau is None else tau
     rows = np.arange(S) if rows is None else np.asarray(rows)
@@ -303,7 +314,7 @@ def expcast_attention_online(q, k, v, tau=None, rows=None, budget=0.0, ph=None, 
             else:
                 Mn = np.asarray(m_trace[c0:c0 + len(r), t], dtype=np.float64)
             f = np.where(np.isinf(M), 0.0, np.exp2(M - Mn))     # exact powers of two
-            P = VALUES[expcast_codes(xt, Mn)]
+            P = VALUES[codes_of(xt, Mn)]
             O = O * f[:, None] + P @ vd[ks]
             L = L * f + P.sum(axis=1)
             M = Mn
@@ -311,7 +322,7 @@ def expcast_attention_online(q, k, v, tau=None, rows=None, budget=0.0, ph=None, 
         O *= float(ph.sv)
         if ph.repair is not None and ph.repair.k > 0:
             rp = ph.repair
-            P = VALUES[expcast_codes(x[:, rp.sel], M)]
+            P = VALUES[codes_of(x[:, rp.sel], M)]
             O += float(rp.sr) * (P @ decode(rp.rc))
         out[c0:c0 + len(r)] = O / L[:, None]
         Ms[c0:c0 + len(r)] = M.astype(np.int64)

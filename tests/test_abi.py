@@ -145,3 +145,17 @@ def test_status_strings():
     for s in range(6):
         assert lib.oc_attn_status_string(s)
     assert lib.oc_attn_last_hip_error() == 0
+
+
+def test_set_weights_accepts_only_the_two_paths():
+    st, p = create(make_desc())
+    assert st == oc.OC_OK
+    try:
+        assert lib.oc_attn_plan_set_weights(p, 0) == oc.OC_OK
+        assert lib.oc_attn_plan_set_weights(p, 1) == oc.OC_OK
+        for bad in (-1, 2, 99):
+            assert lib.oc_attn_plan_set_weights(p, bad) == oc.OC_ERR_INVALID_ARGUMENT
+        assert lib.oc_attn_plan_set_weights(None, 0) == oc.OC_ERR_INVALID_ARGUMENT
+    finally:
+        lib.oc_attn_plan_destroy(p)
+    assert oc.WEIGHTS == {"expcast": 0, "exp_fp8": 1}

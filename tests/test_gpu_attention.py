@@ -23,6 +23,8 @@ from gpu_util import head64, log, oracle_rows, out_rows
 pytestmark = pytest.mark.gpu
 
 TOL = 5e-3
+# oracle byte path -> the kernel's name for it
+KERNEL_WEIGHTS = {"expcast": "expcast", "exp_cast": "exp_fp8"}
 
 
 def _oc():
@@ -62,7 +64,7 @@ def check_max_trace(kernel_trace, own, x, bound, order="mid"):
     return len(bad_rows)
 
 
-def _compare(q, k, v, out, pairs, rows, budget=0.0, tol=TOL, label="", order="mid", prep=None):
+def _compare(q, k, v, out, pairs, rows, budget=0.0, tol=TOL, label="", order="mid", prep=None, weights="expcast"):
     """rel-L2 of the kernel's rows against the single-pass oracle. With a
     prepared workspace, the oracle replays the running-max decisions the
     kernel made (read back through the debug dump), after checking that each
@@ -73,18 +75,18 @@ def _compare(q, k, v, out, pairs, rows, budget=0.0, tol=TOL, label="", order="mi
         m_trace = None
         if prep is not None:
             oc = _oc()
-            _, m_used, _ = oc.debug_pcodes(prep, b, h, with_codes=False)
+            _, m_used, _ = oc.debug_pcodes(prep, b, h, with_codes=False, weights=KERNEL_WEIGHTS[weights])
             m_trace = m_used[torch.as_tensor(rows, device=m_used.device)].cpu().numpy()
-            own = oracle_rows(q, k, v, b, h, rows, budget=budget, order=order)
+            own = oracle_rows(q, k, v, b, h, rows, budget=budget, order=order, weights=weights)
             tau = 1 / math.sqrt(128)
             x = oracle.log2_logits(own["ph"], rows, tau)
             nflip += check_max_trace(m_trace, own["m_trace"], x, logit_error_bound(own["ph"], rows, tau), order)
-        r = oracle_rows(q, k, v, b, h, rows, budget=budget, order=order, m_trace=m_trace)
+        r = oracle_rows(q, k, v, b, h, rows, budget=budget, order=order, m_trace=m_trace, weights=weights)
         got = out_rows(out, b, h, rows)
         e = oracle.rel_l2(got, r["out"])
         errs.append(e)
         r2 = oracle.expcast_attention_head(head64(q, b, h), head64(k, b, h), head64(v, b, h), rows=rows,
-                                           ph=r["ph"])
+                                           ph=r["ph"], weights=weights)
         two.append(oracle.rel_l2(got, r2["out"]))
         assert np.isfinite(got).all()
         assert e <= tol, (label, b, h, e)

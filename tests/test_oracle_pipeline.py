@@ -172,10 +172,11 @@ def test_error_vs_exact_on_small_workload():
 
 # ---- the single-pass (online) form --------------------------------------
 
-def brute_force_online(q, k, v, order, tau=TAU):
+def brute_force_online(q, k, v, order, tau=TAU, weights="expcast"):
     """Online ExpCast attention with explicit loops: key tiles of 128 in the
     given order, running integer max raised before each tile's bytes, running
-    sums multiplied by 2**(M_old - M_new)."""
+    sums multiplied by 2**(M_old - M_new). weights="exp_cast" takes each byte
+    as the E4M3 cast of the fp32 weight 2**(x - M + 8) instead."""
     S, D = len(k), len(k[0])
     qc, kc, sq, sk = [None] * S, [None] * S, [0.0] * S, [0.0] * S
     for x, codes, sc in ((q, qc, sq), (k, kc, sk)):
@@ -202,7 +203,10 @@ def brute_force_online(q, k, v, order, tau=TAU):
                 L, O = L * f, [o * f for o in O]
                 M = Mt
             for j in keys:
-                w = _dec(min(126, max(0, round(8 * (xs[j] - M) + 120 - 0.35))))
+                if weights == "expcast":
+                    w = _dec(min(126, max(0, round(8 * (xs[j] - M) + 120 - 0.35))))
+                else:
+                    w = _dec(_enc(float(np.float32(2.0 ** (xs[j] - M + 8)))))
                 L += w
                 for c in range(D):
                     O[c] += w * vd[j][c]
@@ -231,6 +235,41 @@ def test_online_brute_force_matches_vectorized(S):
         want = brute_force_online(q.tolist(), k.tolist(), v.tolist(), order)[rows]
         got = oracle.expcast_attention_online(q, k, v, rows=rows, order=name)["out"]
         np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("S", [3, 130])
+def test_online_exp_cast_brute_force_matches_vectorized(S):
+    """The comparison path (exponential, fp32, then E4M3 cast) in the online
+    form against explicit loops."""
+    q, k, v = (t[0, :, 0].double().numpy() for t in workloads.random_qkv(1, S, 1, seed=S + 7, scale=2.0))
+    k[S - 1] = q[1] * 1.5
+    k = torch.from_numpy(k).bfloat16().double().numpy()
+    rows = [0, 1, S - 1]
+    nT = -(-S // 128)
+    want = brute_force_online(q.tolist(), k.tolist(), v.tolist(), oracle.key_tile_order(nT), weights="exp_cast")[rows]
+    got = oracle.expcast_attention_online(q, k, v, rows=rows, weights="exp_cast")["out"]
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+    # the two paths write different bytes, so the outputs differ
+    other = oracle.expcast_attention_online(q, k, v, rows=rows)["out"]
+    assert np.abs(other - got).max() > 1e-6
+
+
+def test_exp_cast_path_tracks_exact_weights_closer_than_expcast():
+    """Both byte paths approximate 256*2^(x - M); the exponential path is a
+    plain rounding (ratio within 1 -+ 1/17), ExpCast a shifted one (ratio in
+    [0.929, 1.075]), so the exp path's total variation is the smaller."""
+    rng = np.random.default_rng(3)
+    x = rng.normal(0.0, 2.0, size=(64, 512))
+    M = np.ceil(x.max(axis=1))
+    exact = np.exp2(x - M[:, None])
+    exact /= exact.sum(axis=1, keepdims=True)
+    for codes, bound in ((oracle.exp_cast_codes(x, M), 1 / 17), (oracle.expcast_codes(x, M), 0.0746)):
+        w = oracle.VALUES[codes]
+        normal = codes >= 8
+        ratio = w[normal] / (256.0 * np.exp2(x - M[:, None])[normal])
+        assert np.all(np.abs(ratio - 1) <= bound + 1e-12)
+    tv = lambda c: 0.5 * np.abs(oracle.VALUES[c] / oracle.VALUES[c].sum(axis=1, keepdims=True) - exact).sum(axis=1)  # noqa: E731
+    assert tv(oracle.exp_cast_codes(x, M)).mean() < tv(oracle.expcast_codes(x, M)).mean()
 
 
 def test_online_equals_two_pass_when_max_is_visited_first():
