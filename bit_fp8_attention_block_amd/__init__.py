@@ -10,6 +10,7 @@ fallback path: if the library is missing, importing the binding raises.
     out = attention_v_repair(q, k, v, 0.005)     # full call with V-residual repair
     out = attention_prepared(prep, with_repair=True)   # attention on a prepared workspace
     out = attention_prepared(prep, weights="exp_fp8")  # comparison path: exp + FP8 cast
+    out = attention(q, k, v, k_smooth=True)      # mean key removed before K is quantized
 
 q, k, v: CUDA (HIP) tensors [B,S,H,128] or [S,H,128] in bf16 or fp16, with a
 contiguous channel dimension and 16-byte aligned rows. The output is bf16
@@ -45,14 +46,15 @@ class Desc(ctypes.Structure):
 
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in ("qhat", "kpack", "vpack", "sq", "sk", "vamax", "sv", "energy", "sel",
-                                               "kselpack", "rpack", "sksel", "sr", "total_bytes")] + \
+                                               "kselpack", "rpack", "sksel", "sr", "kmean", "kpart",
+                                               "total_bytes")] + \
                [(n, ctypes.c_int32) for n in ("n_ktiles", "n_qtiles", "s_pad_q", "n_sel_max", "n_sel_tiles_max")]
 
 
 EXPORTS = ("oc_attn_plan_create", "oc_attn_plan_destroy", "oc_attn_workspace_size", "oc_attn_workspace_layout",
            "oc_attn_prepare", "oc_attn_forward", "oc_attn_prepare_v_repair", "oc_attn_forward_v_repair",
            "oc_attn_forward_prepared", "oc_attn_debug_pcodes", "oc_attn_status_string", "oc_attn_last_hip_error",
-           "oc_attn_plan_set_weights")
+           "oc_attn_plan_set_weights", "oc_attn_plan_set_k_smoothing")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -65,6 +67,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.oc_attn_plan_destroy.argtypes = [P]
     lib.oc_attn_plan_destroy.restype = None
     lib.oc_attn_plan_set_weights.argtypes = [P, ctypes.c_int]
+    lib.oc_attn_plan_set_k_smoothing.argtypes = [P, ctypes.c_int]
     lib.oc_attn_workspace_size.argtypes = [P, ctypes.POINTER(SZ)]
     lib.oc_attn_workspace_layout.argtypes = [P, ctypes.POINTER(WsLayout)]
     lib.oc_attn_prepare.argtypes = [P, VP, VP, VP, VP, SZ, VP]
@@ -76,7 +79,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.oc_attn_status_string.argtypes = [st]
     lib.oc_attn_status_string.restype = ctypes.c_char_p
     lib.oc_attn_last_hip_error.argtypes = []
-    for name in ("oc_attn_plan_create", "oc_attn_plan_set_weights", "oc_attn_workspace_size", "oc_attn_workspace_layout", "oc_attn_prepare",
+    for name in ("oc_attn_plan_create", "oc_attn_plan_set_weights", "oc_attn_plan_set_k_smoothing",
+                 "oc_attn_workspace_size", "oc_attn_workspace_layout", "oc_attn_prepare",
                  "oc_attn_forward", "oc_attn_prepare_v_repair", "oc_attn_forward_v_repair",
                  "oc_attn_forward_prepared", "oc_attn_debug_pcodes"):
         getattr(lib, name).restype = st
@@ -99,6 +103,10 @@ def _set_weights(plan, weights):
     if weights not in WEIGHTS:
         raise OcAttnError(OC_ERR_INVALID_ARGUMENT, f"weights must be one of {sorted(WEIGHTS)}")
     _check(_lib.oc_attn_plan_set_weights(plan.handle, WEIGHTS[weights]), "oc_attn_plan_set_weights")
+
+
+def _set_k_smoothing(plan, k_smooth):
+    _check(_lib.oc_attn_plan_set_k_smoothing(plan.handle, int(bool(k_smooth))), "oc_attn_plan_set_k_smoothing")
 
 
 def _ptr(t):
@@ -194,12 +202,14 @@ def _workspace(plan, device):
     return ws
 
 
-def prepare(q, k, v, budget=None, softmax_scale=None) -> Prepared:
+def prepare(q, k, v, budget=None, softmax_scale=None, k_smooth=False) -> Prepared:
     """Quantize q, k, v into a workspace owned by the returned object. With a
     budget (prepare_v_repair), also rank the value tokens by residual energy
-    and quantize the residuals of the top ceil(budget*S) of every (b, h)."""
+    and quantize the residuals of the top ceil(budget*S) of every (b, h).
+    k_smooth subtracts the mean key of every (b, h) before quantizing K."""
     q, k, v, _ = _canon(q, k, v)
     plan = get_plan(q, softmax_scale, budget or 0.0)
+    _set_k_smoothing(plan, k_smooth)
     ws = torch.empty(plan.workspace_bytes + 256, dtype=torch.uint8, device=q.device)
     pad = (-ws.data_ptr()) % 256
     ws = ws[pad:pad + plan.workspace_bytes]
@@ -213,16 +223,18 @@ def prepare(q, k, v, budget=None, softmax_scale=None) -> Prepared:
     return Prepared(plan, ws, tuple(q.shape), q.device, budget, softmax_scale)
 
 
-def prepare_v_repair(q, k, v, budget, softmax_scale=None) -> Prepared:
-    return prepare(q, k, v, budget, softmax_scale)
+def prepare_v_repair(q, k, v, budget, softmax_scale=None, k_smooth=False) -> Prepared:
+    return prepare(q, k, v, budget, softmax_scale, k_smooth)
 
 
-def attention(q, k, v, softmax_scale=None, out=None, weights="expcast"):
+def attention(q, k, v, softmax_scale=None, out=None, weights="expcast", k_smooth=False):
     """Full call: FP8 quantization + ExpCast attention, BF16 output.
-    weights="exp_fp8" runs the comparison path (exponential + FP8 cast)."""
+    weights="exp_fp8" runs the comparison path (exponential + FP8 cast);
+    k_smooth subtracts the mean key before quantizing K."""
     q, k, v, squeeze = _canon(q, k, v)
     plan = get_plan(q, softmax_scale, 0.0)
     _set_weights(plan, weights)
+    _set_k_smoothing(plan, k_smooth)
     ws = _workspace(plan, q.device)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
@@ -231,12 +243,13 @@ def attention(q, k, v, softmax_scale=None, out=None, weights="expcast"):
     return out.squeeze(0) if squeeze else out
 
 
-def attention_v_repair(q, k, v, budget, softmax_scale=None, out=None, weights="expcast"):
+def attention_v_repair(q, k, v, budget, softmax_scale=None, out=None, weights="expcast", k_smooth=False):
     """Full call with V-residual repair of the ceil(budget*S) worst-rounded
     value tokens of every (b, h)."""
     q, k, v, squeeze = _canon(q, k, v)
     plan = get_plan(q, softmax_scale, budget)
     _set_weights(plan, weights)
+    _set_k_smoothing(plan, k_smooth)
     ws = _workspace(plan, q.device)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)

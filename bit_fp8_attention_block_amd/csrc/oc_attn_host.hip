@@ -49,12 +49,14 @@ struct oc_attn_plan {
   int order;
   int grouping;
   int exp_path;          // oc_weights: 0 ExpCast, 1 exp + FP8 cast
+  int k_smooth;          // K-mean smoothing in prepare
   // cached prepare graph
   hipGraphExec_t gexec = nullptr;
   hipStream_t cap_stream = nullptr;
   const void *gq = nullptr, *gk = nullptr, *gv = nullptr;
   void* gws = nullptr;
   int gnsel = -1;
+  int gksmooth = -1;
   // the workspaces this plan prepared most recently, with their repair count
   // (-1: prepared without repair)
   static constexpr int NPREP = 8;
@@ -111,6 +113,8 @@ static void compute_layout(oc_attn_plan* p) {
     L.sksel = take(BH * L.n_sel_tiles_max * (uint64_t)KTILE * 4);
     L.sr = take(BH * 2 * 4);
   }
+  L.kmean = take(BH * HEAD_DIM * 4);
+  L.kpart = take(BH * L.n_ktiles * (uint64_t)HEAD_DIM * 8);
   L.total_bytes = off;
 }
 
@@ -179,6 +183,10 @@ static PrepArgs prep_args(const oc_attn_plan* p, const void* q, const void* k, c
   a.sk = (float*)(base + L.sk);
   a.vamax = (float*)(base + L.vamax);
   a.sv = (float*)(base + L.sv);
+  if (p->k_smooth) {
+    a.kmean = (float*)(base + L.kmean);
+    a.kpart = (double*)(base + L.kpart);
+  }
   if (n_sel > 0) {
     a.energy = (double*)(base + L.energy);
     a.sel = (int32_t*)(base + L.sel);
@@ -239,7 +247,8 @@ static oc_status run_prepare(oc_attn_plan* p, const void* q, const void* k, cons
     e = launch_prepare(a, fp16, st);
     if (e != hipSuccess) return hip_fail(e);
   } else {
-    if (!(p->gexec && p->gq == q && p->gk == k && p->gv == v && p->gws == ws && p->gnsel == n_sel)) {
+    if (!(p->gexec && p->gq == q && p->gk == k && p->gv == v && p->gws == ws && p->gnsel == n_sel &&
+          p->gksmooth == p->k_smooth)) {
       if (p->gexec) {
         (void)hipGraphExecDestroy(p->gexec);
         p->gexec = nullptr;
@@ -269,6 +278,7 @@ static oc_status run_prepare(oc_attn_plan* p, const void* q, const void* k, cons
       p->gv = v;
       p->gws = ws;
       p->gnsel = n_sel;
+      p->gksmooth = p->k_smooth;
     }
     e = hipGraphLaunch(p->gexec, st);
     if (e != hipSuccess) return hip_fail(e);
@@ -317,6 +327,12 @@ oc_status oc_attn_plan_create(const oc_attn_desc* desc, double max_repair_budget
 oc_status oc_attn_plan_set_weights(oc_attn_plan* p, int weights) {
   if (!p || (weights != OC_WEIGHTS_EXPCAST && weights != OC_WEIGHTS_EXP_FP8)) return OC_ERR_INVALID_ARGUMENT;
   p->exp_path = weights == OC_WEIGHTS_EXP_FP8 ? 1 : 0;
+  return OC_OK;
+}
+
+oc_status oc_attn_plan_set_k_smoothing(oc_attn_plan* p, int enable) {
+  if (!p || (enable != 0 && enable != 1)) return OC_ERR_INVALID_ARGUMENT;
+  p->k_smooth = enable;
   return OC_OK;
 }
 

@@ -21,6 +21,9 @@ struct PrepArgs {
   float* sk;
   float* vamax;
   float* sv;                   // [B][H][2]: amax/448, 448/amax
+  // K-mean smoothing (kmean == nullptr: off)
+  float* kmean;                // [B][H][128] fp32 mean key
+  double* kpart;               // [B][H][nT][128] per-block key sums
   // repair (energy == nullptr: no repair)
   double* energy;
   int32_t* sel;

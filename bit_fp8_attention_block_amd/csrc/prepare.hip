@@ -69,11 +69,79 @@ __device__ inline float block_max(float v, float* red) {
   return m;
 }
 
+// 16 fp32 values -> 16 E4M3 bytes of x * inv
+__device__ inline uint4 encode16f(const float (&x)[16], float inv) {
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t p0 = e4m3_encode2(x[4 * i] * inv, x[4 * i + 1] * inv);
+    const uint32_t p1 = e4m3_encode2(x[4 * i + 2] * inv, x[4 * i + 3] * inv);
+    o[i] = p0 | (p1 << 16);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// ---------------------------------------------------------------------------
+// K-mean smoothing, step 1: per (b, h, 128-token block), the float64 sum of
+// the block's keys per channel (exact for bf16/fp16 inputs unless a channel
+// spans more than about 28 binades). grid (nT, H, B), 256 threads.
+template <bool FP16>
+__global__ __launch_bounds__(256) void kmean_partial_kernel(PrepArgs a) {
+  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, rsub = tid >> 3, oc = tid & 7;
+  const int bh = b * a.H + h;
+  __shared__ double part[32][HEAD_DIM + 1];
+  double acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int tok = blk * KTILE + 32 * p + rsub;
+    const int64_t off = (int64_t)b * a.sb + (int64_t)tok * a.ss + (int64_t)h * a.sh + 16 * oc;
+    uint4 lo, hi;
+    load16(a.k + off, tok < a.S, lo, hi);
+    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      acc[2 * i] += (double)half_to_f32<FP16>(w[i] & 0xFFFFu);
+      acc[2 * i + 1] += (double)half_to_f32<FP16>(w[i] >> 16);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) part[rsub][16 * oc + i] = acc[i];
+  __syncthreads();
+  if (tid < HEAD_DIM) {
+    double t = 0.0;
+    for (int r = 0; r < 32; ++r) t += part[r][tid];
+    a.kpart[((int64_t)bh * a.nT + blk) * HEAD_DIM + tid] = t;
+  }
+}
+
+// K-mean smoothing, step 2: per (b, h), kbar = fp32(sum / S) per channel.
+// grid (H, B), 1024 threads: 8 groups of 128 channels take every 8th block,
+// then the 8 group sums are added in group order.
+__global__ __launch_bounds__(1024) void kmean_final_kernel(PrepArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, bh = b * a.H + h;
+  const int g = threadIdx.x >> 7, c = threadIdx.x & (HEAD_DIM - 1);
+  __shared__ double part[8][HEAD_DIM];
+  double t = 0.0;
+  for (int blk = g; blk < a.nT; blk += 8) t += a.kpart[((int64_t)bh * a.nT + blk) * HEAD_DIM + c];
+  part[g][c] = t;
+  __syncthreads();
+  if (g == 0) {
+    double s = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += part[i][c];
+    a.kmean[(int64_t)bh * HEAD_DIM + c] = (float)(s / (double)a.S);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Kernel 1: per (b, h, 128-token block): Q and K block amax, scales, codes;
-// V block amax (the per-head V scale needs all blocks first).
+// V block amax (the per-head V scale needs all blocks first). With
+// KSMOOTH the keys are fp32(k - kbar) before their block amax and codes.
 // grid (nQB, H, B), 256 threads; thread -> rows {32p + tid/8}, channels 16*(tid%8)..+16
-template <bool FP16>
+template <bool FP16, bool KSMOOTH>
 __global__ __launch_bounds__(256) void prep_qk_kernel(PrepArgs a) {
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, rsub = tid >> 3, oc = tid & 7;
@@ -96,8 +164,29 @@ __global__ __launch_bounds__(256) void prep_qk_kernel(PrepArgs a) {
     load16(a.v + off, valid && kv, vl, vh);
     mv = absmax_bits(vl, vh, mv);
   }
+  float ks[KSMOOTH ? 4 : 1][16];
+  float amk_local = bits_to_f32<FP16>(mk);
+  if (KSMOOTH) {
+    float kbar[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) kbar[i] = a.kmean[(int64_t)bh * HEAD_DIM + 16 * oc + i];
+    amk_local = 0.0f;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const bool valid = blk * KTILE + 32 * p + rsub < a.S;
+      const uint32_t w[8] = {kl[p].x, kl[p].y, kl[p].z, kl[p].w, kh[p].x, kh[p].y, kh[p].z, kh[p].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // padding rows stay zero
+        ks[p][2 * i] = valid ? bits_to_f32<FP16>(w[i] & 0xFFFFu) - kbar[2 * i] : 0.0f;
+        ks[p][2 * i + 1] = valid ? bits_to_f32<FP16>(w[i] >> 16) - kbar[2 * i + 1] : 0.0f;
+        amk_local = __builtin_fmaxf(amk_local, __builtin_fmaxf(__builtin_fabsf(ks[p][2 * i]),
+                                                               __builtin_fabsf(ks[p][2 * i + 1])));
+      }
+    }
+  }
   const float amq = block_max(bits_to_f32<FP16>(mq), red);
-  const float amk = block_max(bits_to_f32<FP16>(mk), red + 4);
+  const float amk = block_max(amk_local, red + 4);
   const float amv = block_max(bits_to_f32<FP16>(mv), red + 8);
   float sq, iq, sk, ik;
   quant_scales(amq, sq, iq);
@@ -115,7 +204,12 @@ __global__ __launch_bounds__(256) void prep_qk_kernel(PrepArgs a) {
   for (int p = 0; p < 4; ++p) {
     const int row = 32 * p + rsub;
     *reinterpret_cast<uint4*>(qdst + row * HEAD_DIM + 16 * oc) = encode16<FP16>(ql[p], qh[p], iq);
-    if (kv) *reinterpret_cast<uint4*>(kdst + opidx(row, 16 * oc)) = encode16<FP16>(kl[p], kh[p], ik);
+    if (kv) {
+      uint4 kc;
+      if (KSMOOTH) kc = encode16f(ks[p], ik);
+      else kc = encode16<FP16>(kl[p], kh[p], ik);
+      *reinterpret_cast<uint4*>(kdst + opidx(row, 16 * oc)) = kc;
+    }
   }
 }
 
@@ -393,15 +487,27 @@ __global__ __launch_bounds__(256) void pack_repair_kernel(PrepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-hipError_t launch_prepare(const PrepArgs& a, bool fp16, hipStream_t st) {
+template <bool FP16>
+static void launch_qk(const PrepArgs& a, hipStream_t st) {
   const dim3 g1(a.nQB, a.H, a.B), g2(a.nT, a.H, a.B);
+  if (a.kmean != nullptr) {
+    hipLaunchKernelGGL(kmean_partial_kernel<FP16>, g2, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(kmean_final_kernel, dim3(a.H, a.B), dim3(1024), 0, st, a);
+    hipLaunchKernelGGL((prep_qk_kernel<FP16, true>), g1, dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((prep_qk_kernel<FP16, false>), g1, dim3(256), 0, st, a);
+  }
+}
+
+hipError_t launch_prepare(const PrepArgs& a, bool fp16, hipStream_t st) {
+  const dim3 g2(a.nT, a.H, a.B);
   const bool rep = a.energy != nullptr;
   if (fp16) {
-    hipLaunchKernelGGL(prep_qk_kernel<true>, g1, dim3(256), 0, st, a);
+    launch_qk<true>(a, st);
     if (rep) hipLaunchKernelGGL((prep_v_kernel<true, true>), g2, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((prep_v_kernel<true, false>), g2, dim3(256), 0, st, a);
   } else {
-    hipLaunchKernelGGL(prep_qk_kernel<false>, g1, dim3(256), 0, st, a);
+    launch_qk<false>(a, st);
     if (rep) hipLaunchKernelGGL((prep_v_kernel<false, true>), g2, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((prep_v_kernel<false, false>), g2, dim3(256), 0, st, a);
   }

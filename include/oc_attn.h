@@ -119,10 +119,13 @@ typedef struct oc_attn_desc {
  *    n_sel_tiles = ceil(n_sel/128) of the last prepare_v_repair, inside
  *    space sized for the plan's maximum budget)
  *   sr     f32 [B][H][2]              {amax/448, 448/amax} of the selected residuals
+ *   kmean  f32 [B][H][128]            mean key per channel (K-mean smoothing only)
+ *   kpart  f64 [B][H][n_ktiles][128]  per-block key sums (K-mean smoothing only)
  */
 typedef struct oc_attn_ws_layout {
   uint64_t qhat, kpack, vpack, sq, sk, vamax, sv;
   uint64_t energy, sel, kselpack, rpack, sksel, sr;
+  uint64_t kmean, kpart;
   uint64_t total_bytes;
   int32_t n_ktiles, n_qtiles, s_pad_q, n_sel_max, n_sel_tiles_max;
 } oc_attn_ws_layout;
@@ -150,6 +153,16 @@ void oc_attn_plan_destroy(oc_attn_plan* plan);
  * was. */
 typedef enum oc_weights { OC_WEIGHTS_EXPCAST = 0, OC_WEIGHTS_EXP_FP8 = 1 } oc_weights;
 oc_status oc_attn_plan_set_weights(oc_attn_plan* plan, int weights);
+/* K-mean smoothing for later prepare calls on this plan (host-only; default
+ * off). When on, the prepare step first takes the mean key of every (b, h)
+ * per channel, kbar = fp32(sum_j k_j / S) with the sum in float64, and
+ * quantizes fp32(k - kbar) in place of k. q.(k - kbar) differs from q.k by a
+ * constant per query row, which softmax ignores, while the K blocks lose a
+ * shared bias that would otherwise widen their FP8 range. The pages name Q/K
+ * smoothing as prior practice, not as part of this method (VC-Attention
+ * write-up, section on why attention is the video bottleneck), so it is an
+ * option. enable must be 0 or 1, else OC_ERR_INVALID_ARGUMENT. */
+oc_status oc_attn_plan_set_k_smoothing(oc_attn_plan* plan, int enable);
 /* Workspace bytes the plan needs (host-only). */
 oc_status oc_attn_workspace_size(const oc_attn_plan* plan, size_t* bytes);
 /* Buffer offsets inside the workspace (host-only). */

@@ -35,6 +35,12 @@ Readings where the pages leave a step open (each is listed in the design doc):
   * Q/K scale blocks are 128 tokens x 128 channels; scale s = amax/448 in fp32,
     quantization multiplies by the fp32 reciprocal 448/amax; an all-zero
     block gets s = 1.
+  * K-mean smoothing (an option, off by default; the VC-Attention write-up,
+    section on why attention is the bottleneck, names Q/K smoothing as prior
+    practice): before the K blocks are quantized, every key loses the mean key
+    of its (batch, head), k' = fp32(k - kbar) with kbar = fp32(sum_j k_j / S)
+    per channel. q.k' = q.k - q.kbar shifts each score row by a constant, which
+    softmax ignores.
   * repair: residual r = v - sv*dec(v_hat) in fp32; energy = sum over the 128
     channels of r^2 accumulated in float64 in channel order; the top
     k = ceil(budget*S) tokens by energy (ties to the lower index) are repaired
@@ -143,11 +149,24 @@ def repair_select(v: np.ndarray, vc: np.ndarray, sv, budget: float) -> RepairSet
     return RepairSet(k, sel, energy, quantize_with(rs, inv), sr)
 
 
-def prepare_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, budget: float = 0.0) -> PreparedHead:
+def key_mean(k: np.ndarray) -> np.ndarray:
+    """fp32 mean key over the S tokens, per channel: the float64 sum divided by
+    S, rounded to fp32 (the sum of bf16/fp16 values is exact in float64 unless
+    a channel spans more than about 28 binades)."""
+    return (k.sum(axis=0) / k.shape[0]).astype(F32)
+
+
+def smooth_keys(k: np.ndarray) -> np.ndarray:
+    """K-mean smoothing: fp32(k - kbar), returned as float64."""
+    return (k.astype(F32) - key_mean(k)).astype(np.float64)
+
+
+def prepare_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, budget: float = 0.0,
+                 k_smooth: bool = False) -> PreparedHead:
     """Quantize one (batch, head) slice; inputs are float64 [S, 128] holding
-    bf16/fp16-exact values."""
+    bf16/fp16-exact values. k_smooth subtracts the mean key first."""
     qc, sq = quantize_blocks(q)
-    kc, sk = quantize_blocks(k)
+    kc, sk = quantize_blocks(smooth_keys(k) if k_smooth else k)
     vc, sv = quantize_head(v)
     rep = repair_select(v, vc, sv, budget) if budget > 0 else None
     return PreparedHead(qc, sq, kc, sk, vc, sv, rep)
@@ -193,7 +212,7 @@ def exp_cast_codes(x: np.ndarray, M) -> np.ndarray:
 
 
 def expcast_attention_head(q, k, v, tau=None, rows=None, budget=0.0, ph=None,
-                           quantize=True, weights="expcast", chunk=512):
+                           quantize=True, weights="expcast", chunk=512, k_smooth=False):
     """Output rows of ExpCast attention for one (batch, head) slice.
 
     q, k, v: float64 [S, 128]. Returns a dict with the float64 output rows
@@ -210,7 +229,7 @@ def expcast_attention_head(q, k, v, tau=None, rows=None, budget=0.0, ph=None,
     rows = np.arange(S) if rows is None else np.asarray(rows)
     if ph is None:
         if quantize:
-            ph = prepare_head(q, k, v, budget)
+            ph = prepare_head(q, k, v, budget, k_smooth=k_smooth)
         else:
             ones = lambda n: np.ones(n, dtype=F32)  # noqa: E731
             ph = PreparedHead(None, ones((S + QK_BLOCK - 1) // QK_BLOCK), None,
@@ -262,7 +281,7 @@ def key_tile_order(n_tiles: int) -> list:
 
 
 def expcast_attention_online(q, k, v, tau=None, rows=None, budget=0.0, ph=None, order="mid", chunk=256,
-                             m_trace=None, weights="expcast"):
+                             m_trace=None, weights="expcast", k_smooth=False):
     """Single-pass (flash) form of ExpCast attention, as the pages' kernel runs
     it: keys are consumed in 128-key tiles in `order` ("mid" = key_tile_order,
     "ascending" = 0, 1, 2, ...). Per row, a running bit-aligned max M is raised
@@ -292,7 +311,7 @@ def expcast_attention_online(q, k, v, tau=None, rows=None, budget=0.0, ph=None, 
     tau = 1.0 / math.sqrt(D) if tau is None else tau
     rows = np.arange(S) if rows is None else np.asarray(rows)
     if ph is None:
-        ph = prepare_head(q, k, v, budget)
+        ph = prepare_head(q, k, v, budget, k_smooth=k_smooth)
     nT = (S + QK_BLOCK - 1) // QK_BLOCK
     tiles = key_tile_order(nT) if order == "mid" else list(range(nT))
     vd = decode(ph.vc)

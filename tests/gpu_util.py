@@ -118,18 +118,22 @@ class WsView:
     def sr(self, b, h):
         return self._arr(self.L.sr + 8 * self.bh(b, h), np.float32, 2)
 
+    def kmean(self, b, h):
+        return self._arr(self.L.kmean + 4 * 128 * self.bh(b, h), np.float32, 128)
+
     def energy(self, b, h):
         return self._arr(self.L.energy + 8 * self.bh(b, h) * self.S, np.float64, self.S)
 
 
-def oracle_rows(q, k, v, b, h, rows, budget=0.0, tau=None, order="mid", m_trace=None, weights="expcast"):
+def oracle_rows(q, k, v, b, h, rows, budget=0.0, tau=None, order="mid", m_trace=None, weights="expcast",
+                k_smooth=False):
     """oracle output rows for one (b, h), in the single-pass form the kernel
     computes (key tiles from the middle of the window outwards), plus the
     prepared head; m_trace replays given running-max decisions; weights
     "exp_cast" is the comparison byte path"""
     qh, kh, vh = head64(q, b, h), head64(k, b, h), head64(v, b, h)
     return oracle.expcast_attention_online(qh, kh, vh, tau=tau, rows=rows, budget=budget, order=order,
-                                           m_trace=m_trace, weights=weights)
+                                           m_trace=m_trace, weights=weights, k_smooth=k_smooth)
 
 
 def out_rows(out, b, h, rows):

@@ -159,3 +159,31 @@ def test_set_weights_accepts_only_the_two_paths():
     finally:
         lib.oc_attn_plan_destroy(p)
     assert oc.WEIGHTS == {"expcast": 0, "exp_fp8": 1}
+
+
+def test_set_k_smoothing_accepts_0_and_1():
+    st, p = create(make_desc())
+    assert st == oc.OC_OK
+    try:
+        assert lib.oc_attn_plan_set_k_smoothing(p, 1) == oc.OC_OK
+        assert lib.oc_attn_plan_set_k_smoothing(p, 0) == oc.OC_OK
+        for bad in (-1, 2):
+            assert lib.oc_attn_plan_set_k_smoothing(p, bad) == oc.OC_ERR_INVALID_ARGUMENT
+        assert lib.oc_attn_plan_set_k_smoothing(None, 1) == oc.OC_ERR_INVALID_ARGUMENT
+    finally:
+        lib.oc_attn_plan_destroy(p)
+
+
+def test_k_smoothing_buffers_in_layout():
+    d = make_desc(B=2, S=1000, H=3)
+    st, p = create(d)
+    assert st == oc.OC_OK
+    try:
+        L = oc.WsLayout()
+        assert lib.oc_attn_workspace_layout(p, ctypes.byref(L)) == oc.OC_OK
+        nT = math.ceil(1000 / 128)
+        assert L.kmean % 256 == 0 and L.kpart % 256 == 0
+        assert L.kpart >= L.kmean + 2 * 3 * 128 * 4
+        assert L.total_bytes >= L.kpart + 2 * 3 * nT * 128 * 8
+    finally:
+        lib.oc_attn_plan_destroy(p)

@@ -40,9 +40,14 @@ def _scales(amax):
     return np.float32(a / np.float32(448)), np.float32(np.float32(448) / a)
 
 
-def brute_force(q, k, v, tau=TAU):
-    """ExpCast attention with explicit loops over tokens, channels and keys."""
+def brute_force(q, k, v, tau=TAU, k_smooth=False):
+    """ExpCast attention with explicit loops over tokens, channels and keys.
+    k_smooth: subtract the mean key (exact sum by math.fsum, divided by S,
+    rounded to fp32; fp32 subtraction) before the K blocks are quantized."""
     S, D = len(k), len(k[0])
+    if k_smooth:
+        kbar = [np.float32(math.fsum(k[i][c] for i in range(S)) / S) for c in range(D)]
+        k = [[float(np.float32(k[i][c]) - kbar[c]) for c in range(D)] for i in range(S)]
     qc, kc, sq, sk = [None] * S, [None] * S, [0.0] * S, [0.0] * S
     for x, codes, sc in ((q, qc, sq), (k, kc, sk)):
         for b0 in range(0, S, 128):
@@ -235,6 +240,56 @@ def test_online_brute_force_matches_vectorized(S):
         want = brute_force_online(q.tolist(), k.tolist(), v.tolist(), order)[rows]
         got = oracle.expcast_attention_online(q, k, v, rows=rows, order=name)["out"]
         np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("S", [2, 17, 130])
+def test_k_smoothing_brute_force_matches_vectorized(S):
+    q, k, v = (t[0, :, 0].double().numpy() for t in workloads.random_qkv(1, S, 1, seed=S + 11, scale=2.0))
+    k = torch.from_numpy(k + 5.0 * np.sin(np.arange(128))[None, :]).bfloat16().double().numpy()   # channel bias
+    rows = [0, S - 1]
+    want = brute_force(q.tolist(), k.tolist(), v.tolist(), k_smooth=True)[0][rows]
+    got = oracle.expcast_attention_head(q, k, v, rows=rows, k_smooth=True)["out"]
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+def test_k_smoothing_removes_a_shared_key_offset_exactly():
+    """Keys with zero mean plus a per-channel offset: smoothing takes the
+    offset off exactly, so codes and scales equal those of the offset-free
+    keys, and the outputs agree to rounding (softmax ignores a per-row
+    shift of the scores)."""
+    rng = np.random.default_rng(5)
+    S = 256
+    u = rng.integers(1, 8, size=(S // 2, 128)) / 8.0
+    k0 = np.empty((S, 128))
+    k0[0::2], k0[1::2] = u, -u                        # every column sums to zero
+    c = rng.integers(-9, 10, size=128).astype(np.float64)
+    k = k0 + c                                        # exact in bf16 (at most 8 significant bits)
+    assert np.array_equal(torch.from_numpy(k).bfloat16().double().numpy(), k)
+    q = torch.from_numpy(rng.normal(size=(S, 128))).bfloat16().double().numpy()
+    v = torch.from_numpy(rng.normal(size=(S, 128))).bfloat16().double().numpy()
+    np.testing.assert_array_equal(oracle.key_mean(k), c.astype(np.float32))
+    a = oracle.prepare_head(q, k, v, k_smooth=True)
+    b = oracle.prepare_head(q, k0, v)
+    np.testing.assert_array_equal(a.kc, b.kc)
+    np.testing.assert_array_equal(a.sk, b.sk)
+    # without smoothing the offset changes the K codes
+    assert not np.array_equal(oracle.prepare_head(q, k, v).kc, b.kc)
+
+
+def test_k_smoothing_lowers_error_on_biased_keys():
+    """A large per-channel key bias wastes the FP8 range of every K block;
+    removing the mean brings the error against exact attention down."""
+    rng = np.random.default_rng(6)
+    S = 1024
+    q = rng.normal(size=(S, 128)) + rng.normal(0, math.sqrt(3), size=128)
+    k = rng.normal(size=(S, 128)) + rng.normal(0, math.sqrt(3), size=128)
+    v = rng.normal(size=(S, 128))
+    q, k, v = (torch.from_numpy(t).bfloat16().double().numpy() for t in (q, k, v))
+    rows = np.arange(0, S, 4)
+    exact = oracle.exact_attention_head(q, k, v, rows=rows)
+    plain = oracle.rel_l2(oracle.expcast_attention_head(q, k, v, rows=rows)["out"], exact)
+    smooth = oracle.rel_l2(oracle.expcast_attention_head(q, k, v, rows=rows, k_smooth=True)["out"], exact)
+    assert smooth < 0.8 * plain, (plain, smooth)
 
 
 @pytest.mark.parametrize("S", [3, 130])
