@@ -40,7 +40,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 # rocprofv3 PMC counters (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors a
 # plain 4 GiB copy gives; profiles/attn_kernel_s73397_h56.md). They are only
 # reported while the kernel sources still hash to the measured version.
-MEASURED_TRAFFIC = {"sources_sha256": "c03354e327efb7930c8557a1bf410fa71d6b6269b5e3d3aee6430f9b40408bde", "bytes": 22556986181}
+MEASURED_TRAFFIC = {"sources_sha256": "099ab3591a753edcd6bf1715a923efb5d842ccede358d38e9645cdd4e8a3fa08", "bytes": 11964233301}
 KERNEL_SOURCES = ("bit_fp8_attention_block_amd/csrc/attention.hip", "bit_fp8_attention_block_amd/csrc/oc_common.h")
 
 
@@ -124,6 +124,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparator", action="store_true")
     ap.add_argument("--kernel-only", action="store_true", help="time only the attention kernel (for profiling)")
+    ap.add_argument("--weights", default="expcast", choices=("expcast", "exp_fp8"),
+                    help="byte path of the kernel timed by --kernel-only")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -157,10 +159,12 @@ def main():
     prep = oc.prepare_v_repair(q, k, v, max(args.budget, args.repair_budget))
     out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     log("[bench] attention kernel alone")
-    k_ms, _ = timed_calls(lambda: oc.attention_prepared(prep, with_repair=False, out=out), args.steps, args.warmup)
     if args.kernel_only:
-        print(json.dumps({"kernel_ms": k_ms, "kernel_tflops": flop / k_ms / 1e9}))
+        k_ms, _ = timed_calls(lambda: oc.attention_prepared(prep, with_repair=False, out=out, weights=args.weights),
+                              args.steps, args.warmup)
+        print(json.dumps({"kernel_ms": k_ms, "kernel_tflops": flop / k_ms / 1e9, "weights": args.weights}))
         return
+    k_ms, _ = timed_calls(lambda: oc.attention_prepared(prep, with_repair=False, out=out), args.steps, args.warmup)
     kr_ms, _ = timed_calls(lambda: oc.attention_prepared(prep, with_repair=True, out=out), args.steps, 1)
     # the same kernel on the byte path ExpCast replaces (exponential + FP8 cast)
     log("[bench] attention kernel alone, exponential + FP8-cast weights")
@@ -192,6 +196,10 @@ def main():
     st = lambda: oc._lib.oc_attn_prepare(plan.handle, oc._ptr(q), oc._ptr(k), oc._ptr(v), oc._ptr(ws),  # noqa: E731
                                          ws.numel(), oc._stream(dev))
     p_ms, _ = timed_calls(st, args.steps, 1)
+    # the same prepare with K-mean smoothing (two more small kernels, K read twice)
+    oc._lib.oc_attn_plan_set_k_smoothing(plan.handle, 1)
+    pks_ms, _ = timed_calls(st, args.steps, 1)
+    oc._lib.oc_attn_plan_set_k_smoothing(plan.handle, 0)
     in_bytes = 3 * 2 * w.B * w.S * w.H * 128
     prep_bytes = in_bytes + in_bytes // 2 + (in_bytes // 3)   # read q,k,v + V again; write 3 FP8 tensors
     sdpa_ms = None if args.no_comparator else bf16_comparator(q, k, v, max(2, min(args.steps, 3)))
@@ -232,6 +240,7 @@ def main():
         "full_call_ms_events": round(full_ev_ms, 4),
         "prepare_ms": round(p_ms, 4),
         "prepare_gbs": round(prep_bytes / p_ms / 1e6, 1),
+        "prepare_k_smooth_ms": round(pks_ms, 4),
         "full_call_repair_ms": round(rep_ms, 4),
         "repair_budget_measured": args.repair_budget,
         "bf16_sdpa_ms": None if sdpa_ms is None else round(sdpa_ms, 3),
