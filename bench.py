@@ -14,8 +14,8 @@ is one JSON record:
                same workload on this host's cores
 plus the prepare time, the repaired call, the same attention kernel on the
 byte path ExpCast replaces (one exponential per score, then the FP32->FP8
-cast), and a BF16 attention run through torch's SDPA on the same GPU for
-comparison. Progress goes to stderr.
+cast) and on a V-Smooth workspace, and a BF16 attention run through torch's
+SDPA on the same GPU for comparison. Progress goes to stderr.
 """
 from __future__ import annotations
 
@@ -171,6 +171,11 @@ def main():
     ke_ms, _ = timed_calls(lambda: oc.attention_prepared(prep, with_repair=False, out=out, weights="exp_fp8"),
                            args.steps, 1)
     del prep
+    # the same kernel on a V-Smooth workspace (block means added back per key tile)
+    log("[bench] attention kernel alone, V-Smooth workspace")
+    prep_vs = oc.prepare(q, k, v, v_smooth=True)
+    kvs_ms, _ = timed_calls(lambda: oc.attention_prepared(prep_vs, out=out), args.steps, 1)
+    del prep_vs
 
     # full call (prepare graph + attention), the headline step
     log("[bench] full call")
@@ -237,6 +242,7 @@ def main():
         "kernel_repair_ms": round(kr_ms, 4),
         "kernel_exp_fp8_ms": round(ke_ms, 4),
         "expcast_speedup_vs_exp_fp8": round(ke_ms / k_ms, 3),
+        "kernel_v_smooth_ms": round(kvs_ms, 4),
         "full_call_ms_events": round(full_ev_ms, 4),
         "prepare_ms": round(p_ms, 4),
         "prepare_gbs": round(prep_bytes / p_ms / 1e6, 1),

@@ -11,6 +11,7 @@ fallback path: if the library is missing, importing the binding raises.
     out = attention_prepared(prep, with_repair=True)   # attention on a prepared workspace
     out = attention_prepared(prep, weights="exp_fp8")  # comparison path: exp + FP8 cast
     out = attention(q, k, v, k_smooth=True)      # mean key removed before K is quantized
+    out = attention(q, k, v, v_smooth=True)      # V as residuals from its 128-token block means
 
 q, k, v: CUDA (HIP) tensors [B,S,H,128] or [S,H,128] in bf16 or fp16, with a
 contiguous channel dimension and 16-byte aligned rows. The output is bf16
@@ -46,7 +47,7 @@ class Desc(ctypes.Structure):
 
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in ("qhat", "kpack", "vpack", "sq", "sk", "vamax", "sv", "energy", "sel",
-                                               "kselpack", "rpack", "sksel", "sr", "kmean", "kpart",
+                                               "kselpack", "rpack", "sksel", "sr", "kmean", "kpart", "vmu", "vmus",
                                                "total_bytes")] + \
                [(n, ctypes.c_int32) for n in ("n_ktiles", "n_qtiles", "s_pad_q", "n_sel_max", "n_sel_tiles_max")]
 
@@ -54,7 +55,7 @@ class WsLayout(ctypes.Structure):
 EXPORTS = ("oc_attn_plan_create", "oc_attn_plan_destroy", "oc_attn_workspace_size", "oc_attn_workspace_layout",
            "oc_attn_prepare", "oc_attn_forward", "oc_attn_prepare_v_repair", "oc_attn_forward_v_repair",
            "oc_attn_forward_prepared", "oc_attn_debug_pcodes", "oc_attn_status_string", "oc_attn_last_hip_error",
-           "oc_attn_plan_set_weights", "oc_attn_plan_set_k_smoothing")
+           "oc_attn_plan_set_weights", "oc_attn_plan_set_k_smoothing", "oc_attn_plan_set_v_smoothing")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -68,6 +69,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.oc_attn_plan_destroy.restype = None
     lib.oc_attn_plan_set_weights.argtypes = [P, ctypes.c_int]
     lib.oc_attn_plan_set_k_smoothing.argtypes = [P, ctypes.c_int]
+    lib.oc_attn_plan_set_v_smoothing.argtypes = [P, ctypes.c_int]
     lib.oc_attn_workspace_size.argtypes = [P, ctypes.POINTER(SZ)]
     lib.oc_attn_workspace_layout.argtypes = [P, ctypes.POINTER(WsLayout)]
     lib.oc_attn_prepare.argtypes = [P, VP, VP, VP, VP, SZ, VP]
@@ -80,6 +82,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.oc_attn_status_string.restype = ctypes.c_char_p
     lib.oc_attn_last_hip_error.argtypes = []
     for name in ("oc_attn_plan_create", "oc_attn_plan_set_weights", "oc_attn_plan_set_k_smoothing",
+                 "oc_attn_plan_set_v_smoothing",
                  "oc_attn_workspace_size", "oc_attn_workspace_layout", "oc_attn_prepare",
                  "oc_attn_forward", "oc_attn_prepare_v_repair", "oc_attn_forward_v_repair",
                  "oc_attn_forward_prepared", "oc_attn_debug_pcodes"):
@@ -105,8 +108,9 @@ def _set_weights(plan, weights):
     _check(_lib.oc_attn_plan_set_weights(plan.handle, WEIGHTS[weights]), "oc_attn_plan_set_weights")
 
 
-def _set_k_smoothing(plan, k_smooth):
+def _set_smoothing(plan, k_smooth, v_smooth):
     _check(_lib.oc_attn_plan_set_k_smoothing(plan.handle, int(bool(k_smooth))), "oc_attn_plan_set_k_smoothing")
+    _check(_lib.oc_attn_plan_set_v_smoothing(plan.handle, int(bool(v_smooth))), "oc_attn_plan_set_v_smoothing")
 
 
 def _ptr(t):
@@ -202,14 +206,15 @@ def _workspace(plan, device):
     return ws
 
 
-def prepare(q, k, v, budget=None, softmax_scale=None, k_smooth=False) -> Prepared:
+def prepare(q, k, v, budget=None, softmax_scale=None, k_smooth=False, v_smooth=False) -> Prepared:
     """Quantize q, k, v into a workspace owned by the returned object. With a
     budget (prepare_v_repair), also rank the value tokens by residual energy
     and quantize the residuals of the top ceil(budget*S) of every (b, h).
-    k_smooth subtracts the mean key of every (b, h) before quantizing K."""
+    k_smooth subtracts the mean key of every (b, h) before quantizing K;
+    v_smooth quantizes V as residuals from its 128-token block means."""
     q, k, v, _ = _canon(q, k, v)
     plan = get_plan(q, softmax_scale, budget or 0.0)
-    _set_k_smoothing(plan, k_smooth)
+    _set_smoothing(plan, k_smooth, v_smooth)
     ws = torch.empty(plan.workspace_bytes + 256, dtype=torch.uint8, device=q.device)
     pad = (-ws.data_ptr()) % 256
     ws = ws[pad:pad + plan.workspace_bytes]
@@ -223,18 +228,19 @@ def prepare(q, k, v, budget=None, softmax_scale=None, k_smooth=False) -> Prepare
     return Prepared(plan, ws, tuple(q.shape), q.device, budget, softmax_scale)
 
 
-def prepare_v_repair(q, k, v, budget, softmax_scale=None, k_smooth=False) -> Prepared:
-    return prepare(q, k, v, budget, softmax_scale, k_smooth)
+def prepare_v_repair(q, k, v, budget, softmax_scale=None, k_smooth=False, v_smooth=False) -> Prepared:
+    return prepare(q, k, v, budget, softmax_scale, k_smooth, v_smooth)
 
 
-def attention(q, k, v, softmax_scale=None, out=None, weights="expcast", k_smooth=False):
+def attention(q, k, v, softmax_scale=None, out=None, weights="expcast", k_smooth=False, v_smooth=False):
     """Full call: FP8 quantization + ExpCast attention, BF16 output.
     weights="exp_fp8" runs the comparison path (exponential + FP8 cast);
-    k_smooth subtracts the mean key before quantizing K."""
+    k_smooth subtracts the mean key before quantizing K; v_smooth quantizes V
+    as residuals from its block means and adds the means back per key tile."""
     q, k, v, squeeze = _canon(q, k, v)
     plan = get_plan(q, softmax_scale, 0.0)
     _set_weights(plan, weights)
-    _set_k_smoothing(plan, k_smooth)
+    _set_smoothing(plan, k_smooth, v_smooth)
     ws = _workspace(plan, q.device)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
@@ -243,13 +249,14 @@ def attention(q, k, v, softmax_scale=None, out=None, weights="expcast", k_smooth
     return out.squeeze(0) if squeeze else out
 
 
-def attention_v_repair(q, k, v, budget, softmax_scale=None, out=None, weights="expcast", k_smooth=False):
+def attention_v_repair(q, k, v, budget, softmax_scale=None, out=None, weights="expcast", k_smooth=False,
+                       v_smooth=False):
     """Full call with V-residual repair of the ceil(budget*S) worst-rounded
     value tokens of every (b, h)."""
     q, k, v, squeeze = _canon(q, k, v)
     plan = get_plan(q, softmax_scale, budget)
     _set_weights(plan, weights)
-    _set_k_smoothing(plan, k_smooth)
+    _set_smoothing(plan, k_smooth, v_smooth)
     ws = _workspace(plan, q.device)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)

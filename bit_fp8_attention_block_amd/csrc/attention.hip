@@ -125,6 +125,20 @@ constexpr int NWAVES = 8;         // 2 waves per SIMD: one of each group
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int NBUF = 4;                    // K and V tiles, four buffers each
 constexpr int LDS_BYTES = 2 * NBUF * TILE_BYTES;
+// V-Smooth: the tile's scaled block means (128 fp32 = 512 B) ride with each V
+// tile in a 1 KiB slot
+constexpr int MU_SLOT = 1024;
+constexpr int LDS_BYTES_VS = LDS_BYTES + NBUF * MU_SLOT;
+
+// The 512 bytes of one tile's scaled block means into a 1 KiB LDS slot by one
+// wave's direct load (lanes 32-63 repeat lanes 0-31 into the upper half).
+__device__ inline void load_means(uint8_t* lds_dst, const uint8_t* src, int lane) {
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_dst;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src + (lane & 31) * 16)
+               : "memory", "m0");
+}
 
 // scheduling-group masks of __builtin_amdgcn_sched_group_barrier
 constexpr int SG_MFMA = 0x008, SG_VALU = 0x002, SG_DS_READ = 0x100;
@@ -151,7 +165,8 @@ __device__ __forceinline__ void qk_tile(const uint8_t* kt, const v8i (&qop)[QBW]
   __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2 * QBW, 0);
 }
 
-// O^T += V^T P^T and L += 1 * P^T for one tile, with the same read-ahead
+// O^T += V^T P^T and (ROWSUM) L += 1 * P^T for one tile, with the same read-ahead
+template <bool ROWSUM = true>
 __device__ __forceinline__ void pv_tile(const uint8_t* vt, const v8i (&P)[QBW], v4f (&O)[QBW][8], v4f (&L)[QBW],
                                         int lane) {
   v8i ones;
@@ -166,15 +181,44 @@ __device__ __forceinline__ void pv_tile(const uint8_t* vt, const v8i (&P)[QBW], 
 #pragma unroll
     for (int qb = 0; qb < QBW; ++qb) O[qb][n] = mfma_f8(vop[n], P[qb], O[qb][n]);
   }
+  if (ROWSUM) {
 #pragma unroll
-  for (int qb = 0; qb < QBW; ++qb) L[qb] = mfma_f8(ones, P[qb], L[qb]);
+    for (int qb = 0; qb < QBW; ++qb) L[qb] = mfma_f8(ones, P[qb], L[qb]);
+  }
   __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
 #pragma unroll
   for (int n = 0; n < 6; ++n) {
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, QBW, 0);
     __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(SG_MFMA, 3 * QBW, 0);
+  __builtin_amdgcn_sched_group_barrier(SG_MFMA, ROWSUM ? 3 * QBW : 2 * QBW, 0);
+}
+
+// V-Smooth restore for one tile: its row sum l = 1 * P^T (MFMA; every lane
+// gets the sum of its query), L += l, and O^T[d][q] += (mu_d * inv) * l_q for
+// the tile's block means (the output is multiplied by sv = 1/inv at the end).
+// mu holds the 128 scaled means in lane order: slot 32g + 4n + r is channel
+// 16n + 4g + r, so lane l reads the 32 values of its group g = l/16.
+__device__ __forceinline__ void vsmooth_tile(const uint8_t* mu, const v8i (&P)[QBW], v4f (&O)[QBW][8],
+                                             v4f (&L)[QBW], int g) {
+  v8i ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = 0x38383838;
+  v4f l[QBW];
+#pragma unroll
+  for (int qb = 0; qb < QBW; ++qb) {
+    l[qb] = mfma_f8(ones, P[qb], v4f{0.f, 0.f, 0.f, 0.f});
+    L[qb] += l[qb];
+  }
+  const v4f* m = reinterpret_cast<const v4f*>(mu + 128 * g);
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const v4f mn = m[n];
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) O[qb][n][r] = __builtin_fmaf(mn[r], l[qb][0], O[qb][n][r]);
+  }
 }
 
 // NaN-propagating maximum: scores are finite or -inf, and unlike fmaxf this
@@ -310,11 +354,12 @@ __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], co
 // in iteration s (K s+3, V s+2) may stay in flight until the end of
 // iteration s+1, which hides L2 misses; so K and V get four LDS buffers each
 // (128 KiB).
-template <bool REPAIR, bool DUMP, bool EXPP>
+template <bool REPAIR, bool DUMP, bool EXPP, bool VSMOOTH>
 __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   uint8_t* const kbuf = smem;
   uint8_t* const vbuf = smem + NBUF * TILE_BYTES;
+  uint8_t* const mubuf = smem + 2 * NBUF * TILE_BYTES;   // V-Smooth only
 
   int b, h, qt;
   if (DUMP) {
@@ -380,6 +425,14 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
     if (i < nT) load_tile<NTHREADS>(vbuf + i * TILE_BYTES, vt_ptr(i));
+  const auto mu_ptr = [&](int step) {
+    return reinterpret_cast<const uint8_t*>(a.vmus + ((int64_t)bh * nT + tile_at(step, centre, nT, a.order)) * HEAD_DIM);
+  };
+  if (VSMOOTH && wv == 0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (i < nT) load_means(mubuf + i * MU_SLOT, mu_ptr(i), lane);
+  }
   __builtin_amdgcn_s_waitcnt(0);   // this wave's chunks are in LDS
   __syncthreads();
   if (!group_b) qk_tile(kbuf, qop, S, lane);
@@ -390,28 +443,39 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
     const bool ld_k = s + 3 < nT, ld_v = s + 2 < nT;
     if (ld_k && !group_b) load_tile<NTHREADS / 2>(kbuf + ((s + 3) & (NBUF - 1)) * TILE_BYTES, kt_ptr(s + 3));
     if (ld_v && !group_b) load_tile<NTHREADS / 2>(vbuf + ((s + 2) & (NBUF - 1)) * TILE_BYTES, vt_ptr(s + 2));
+    const bool ld_mu = VSMOOTH && ld_v && wv == 0;
+    if (ld_mu) load_means(mubuf + ((s + 2) & (NBUF - 1)) * MU_SLOT, mu_ptr(s + 2), lane);
     const float skj = skp[j];
     if (!group_b) {
       expcast_tile<DUMP, EXPP>(S, P, aq, skj, M, O, L, j, j == last_masked, a, g, qrow0);
-      pv_tile(vbuf + b0 * TILE_BYTES, P, O, L, lane);
+      if (VSMOOTH) vsmooth_tile(mubuf + b0 * MU_SLOT, P, O, L, g);
+      pv_tile<!VSMOOTH>(vbuf + b0 * TILE_BYTES, P, O, L, lane);
       if (s + 1 < nT) qk_tile(kbuf + b1 * TILE_BYTES, qop, S, lane);
     } else {
       __builtin_amdgcn_s_setprio(2);
       qk_tile(kbuf + b0 * TILE_BYTES, qop, S, lane);
-      if (s > 0) pv_tile(vbuf + bm1 * TILE_BYTES, P, O, L, lane);
+      if (s > 0) pv_tile<!VSMOOTH>(vbuf + bm1 * TILE_BYTES, P, O, L, lane);
       __builtin_amdgcn_s_setprio(0);
       expcast_tile<DUMP, EXPP>(S, P, aq, skj, M, O, L, j, j == last_masked, a, g, qrow0);
+      if (VSMOOTH) vsmooth_tile(mubuf + b0 * MU_SLOT, P, O, L, g);
     }
     // group A waits for the loads it issued one iteration ago (a tile is 4
-    // loads per thread); this iteration's stay in flight. The code dump's
-    // stores also count, so that path drains everything.
+    // loads per thread, plus one for the block means on wave 0 with
+    // V-Smooth); this iteration's stay in flight. The code dump's stores also
+    // count, so that path drains everything.
     if (DUMP || group_b) __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0)
-    else if (ld_k && ld_v) __builtin_amdgcn_s_waitcnt(0x0F78);              // vmcnt(8)
-    else if (ld_k || ld_v) __builtin_amdgcn_s_waitcnt(0x0F74);              // vmcnt(4)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);
+    else if (ld_k && ld_v) {
+      if (ld_mu) __builtin_amdgcn_s_waitcnt(0x0F79);                        // vmcnt(9)
+      else __builtin_amdgcn_s_waitcnt(0x0F78);                              // vmcnt(8)
+    } else if (ld_k || ld_v) {
+      if (ld_mu) __builtin_amdgcn_s_waitcnt(0x0F75);                        // vmcnt(5)
+      else __builtin_amdgcn_s_waitcnt(0x0F74);                              // vmcnt(4)
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
     lds_barrier();
   }
-  if (group_b) pv_tile(vbuf + ((nT - 1) & (NBUF - 1)) * TILE_BYTES, P, O, L, lane);
+  if (group_b) pv_tile<!VSMOOTH>(vbuf + ((nT - 1) & (NBUF - 1)) * TILE_BYTES, P, O, L, lane);
   __builtin_amdgcn_s_waitcnt(0);
 
   float scale = a.sv[2 * bh];
@@ -493,29 +557,34 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   }
 }
 
-template <bool REPAIR, bool DUMP, bool EXPP>
+template <bool REPAIR, bool DUMP, bool EXPP, bool VSMOOTH>
 static hipError_t launch_one(const AttnArgs& a, dim3 grid, hipStream_t st) {
+  constexpr int lds = VSMOOTH ? LDS_BYTES_VS : LDS_BYTES;
   static bool configured = false;
   if (!configured) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<REPAIR, DUMP, EXPP>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<REPAIR, DUMP, EXPP, VSMOOTH>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     configured = true;
   }
-  hipLaunchKernelGGL((attn_kernel<REPAIR, DUMP, EXPP>), grid, dim3(NTHREADS), LDS_BYTES, st, a);
+  hipLaunchKernelGGL((attn_kernel<REPAIR, DUMP, EXPP, VSMOOTH>), grid, dim3(NTHREADS), lds, st, a);
   return hipGetLastError();
 }
 
-template <bool EXPP>
-static hipError_t launch_weights(const AttnArgs& a, bool repair, bool dump, dim3 grid, hipStream_t st) {
-  if (dump) return launch_one<false, true, EXPP>(a, grid, st);
-  return repair ? launch_one<true, false, EXPP>(a, grid, st) : launch_one<false, false, EXPP>(a, grid, st);
+template <bool EXPP, bool VSMOOTH>
+static hipError_t launch_variant(const AttnArgs& a, bool repair, bool dump, dim3 grid, hipStream_t st) {
+  if (dump) return launch_one<false, true, EXPP, VSMOOTH>(a, grid, st);
+  return repair ? launch_one<true, false, EXPP, VSMOOTH>(a, grid, st) : launch_one<false, false, EXPP, VSMOOTH>(a, grid, st);
 }
 
 hipError_t launch_attention(const AttnArgs& a, bool repair, bool dump, hipStream_t st) {
   const int nwork = a.B * a.H * a.nQT;
   const dim3 grid = dump ? dim3(a.nQT) : dim3(8 * ((nwork + 7) / 8));
-  return a.exp_path ? launch_weights<true>(a, repair, dump, grid, st) : launch_weights<false>(a, repair, dump, grid, st);
+  if (a.vmus != nullptr)
+    return a.exp_path ? launch_variant<true, true>(a, repair, dump, grid, st)
+                      : launch_variant<false, true>(a, repair, dump, grid, st);
+  return a.exp_path ? launch_variant<true, false>(a, repair, dump, grid, st)
+                    : launch_variant<false, false>(a, repair, dump, grid, st);
 }
 
 }  // namespace oc

@@ -50,6 +50,7 @@ struct oc_attn_plan {
   int grouping;
   int exp_path;          // oc_weights: 0 ExpCast, 1 exp + FP8 cast
   int k_smooth;          // K-mean smoothing in prepare
+  int v_smooth;          // V-Smooth block means (prepare and attention)
   // cached prepare graph
   hipGraphExec_t gexec = nullptr;
   hipStream_t cap_stream = nullptr;
@@ -57,21 +58,25 @@ struct oc_attn_plan {
   void* gws = nullptr;
   int gnsel = -1;
   int gksmooth = -1;
+  int gvsmooth = -1;
   // the workspaces this plan prepared most recently, with their repair count
   // (-1: prepared without repair)
   static constexpr int NPREP = 8;
   const void* prepared_ws[NPREP] = {};
   int prepared_nsel[NPREP] = {};
+  int prepared_vs[NPREP] = {};
   int prepared_next = 0;
 
-  void mark_prepared(const void* ws, int nsel) {
+  void mark_prepared(const void* ws, int nsel, int vs) {
     for (int i = 0; i < NPREP; ++i)
       if (prepared_ws[i] == ws) {
         prepared_nsel[i] = nsel;
+        prepared_vs[i] = vs;
         return;
       }
     prepared_ws[prepared_next] = ws;
     prepared_nsel[prepared_next] = nsel;
+    prepared_vs[prepared_next] = vs;
     prepared_next = (prepared_next + 1) % NPREP;
   }
   // repair count the workspace was prepared with; -2 if this plan never prepared it
@@ -79,6 +84,13 @@ struct oc_attn_plan {
     for (int i = 0; i < NPREP; ++i)
       if (prepared_ws[i] == ws) return prepared_nsel[i];
     return -2;
+  }
+  // whether the workspace holds V-Smooth residuals (the attention kernel must
+  // then add the block means back)
+  int prepared_vsmooth(const void* ws) const {
+    for (int i = 0; i < NPREP; ++i)
+      if (prepared_ws[i] == ws) return prepared_vs[i];
+    return 0;
   }
 };
 
@@ -115,6 +127,8 @@ static void compute_layout(oc_attn_plan* p) {
   }
   L.kmean = take(BH * HEAD_DIM * 4);
   L.kpart = take(BH * L.n_ktiles * (uint64_t)HEAD_DIM * 8);
+  L.vmu = take(BH * L.n_ktiles * (uint64_t)HEAD_DIM * 2);
+  L.vmus = take(BH * L.n_ktiles * (uint64_t)HEAD_DIM * 4);
   L.total_bytes = off;
 }
 
@@ -187,6 +201,10 @@ static PrepArgs prep_args(const oc_attn_plan* p, const void* q, const void* k, c
     a.kmean = (float*)(base + L.kmean);
     a.kpart = (double*)(base + L.kpart);
   }
+  if (p->v_smooth) {
+    a.vmu = (uint16_t*)(base + L.vmu);
+    a.vmus = (float*)(base + L.vmus);
+  }
   if (n_sel > 0) {
     a.energy = (double*)(base + L.energy);
     a.sel = (int32_t*)(base + L.sel);
@@ -232,6 +250,7 @@ static AttnArgs attn_args(const oc_attn_plan* p, const void* ws, void* out, int 
   a.order = p->order;
   a.grouping = p->grouping;
   a.exp_path = p->exp_path;
+  a.vmus = p->prepared_vsmooth(ws) ? (const float*)(base + L.vmus) : nullptr;
   return a;
 }
 
@@ -248,7 +267,7 @@ static oc_status run_prepare(oc_attn_plan* p, const void* q, const void* k, cons
     if (e != hipSuccess) return hip_fail(e);
   } else {
     if (!(p->gexec && p->gq == q && p->gk == k && p->gv == v && p->gws == ws && p->gnsel == n_sel &&
-          p->gksmooth == p->k_smooth)) {
+          p->gksmooth == p->k_smooth && p->gvsmooth == p->v_smooth)) {
       if (p->gexec) {
         (void)hipGraphExecDestroy(p->gexec);
         p->gexec = nullptr;
@@ -279,11 +298,12 @@ static oc_status run_prepare(oc_attn_plan* p, const void* q, const void* k, cons
       p->gws = ws;
       p->gnsel = n_sel;
       p->gksmooth = p->k_smooth;
+      p->gvsmooth = p->v_smooth;
     }
     e = hipGraphLaunch(p->gexec, st);
     if (e != hipSuccess) return hip_fail(e);
   }
-  p->mark_prepared(ws, n_sel);
+  p->mark_prepared(ws, n_sel, p->v_smooth);
   return OC_OK;
 }
 
@@ -327,6 +347,12 @@ oc_status oc_attn_plan_create(const oc_attn_desc* desc, double max_repair_budget
 oc_status oc_attn_plan_set_weights(oc_attn_plan* p, int weights) {
   if (!p || (weights != OC_WEIGHTS_EXPCAST && weights != OC_WEIGHTS_EXP_FP8)) return OC_ERR_INVALID_ARGUMENT;
   p->exp_path = weights == OC_WEIGHTS_EXP_FP8 ? 1 : 0;
+  return OC_OK;
+}
+
+oc_status oc_attn_plan_set_v_smoothing(oc_attn_plan* p, int enable) {
+  if (!p || (enable != 0 && enable != 1)) return OC_ERR_INVALID_ARGUMENT;
+  p->v_smooth = enable;
   return OC_OK;
 }
 

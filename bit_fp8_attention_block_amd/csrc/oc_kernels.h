@@ -24,6 +24,9 @@ struct PrepArgs {
   // K-mean smoothing (kmean == nullptr: off)
   float* kmean;                // [B][H][128] fp32 mean key
   double* kpart;               // [B][H][nT][128] per-block key sums
+  // V-Smooth block means (vmu == nullptr: off)
+  uint16_t* vmu;               // [B][H][nT][128] bf16 block means
+  float* vmus;                 // [B][H][nT][128] mean * (448/amax), in attention lane order
   // repair (energy == nullptr: no repair)
   double* energy;
   int32_t* sel;
@@ -52,6 +55,7 @@ struct AttnArgs {
   int order;                   // 0: from the middle of the key window outwards, 1: ascending
   int grouping;                // which waves pair up on a SIMD: 0 = w and w+4, 1 = 2i and 2i+1
   int exp_path;                // 0: ExpCast bytes; 1: exp2 + FP32->E4M3 cast (comparison path)
+  const float* vmus;           // V-Smooth: [B][H][nT][128] scaled block means (nullptr: off)
   uint8_t* dump_codes;         // debug: [S][S] bytes for one (b, h)
   int32_t* dump_m;             // debug: [S][nT]
   int dump_b, dump_h;

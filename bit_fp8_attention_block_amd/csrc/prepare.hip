@@ -140,8 +140,11 @@ __global__ __launch_bounds__(1024) void kmean_final_kernel(PrepArgs a) {
 // Kernel 1: per (b, h, 128-token block): Q and K block amax, scales, codes;
 // V block amax (the per-head V scale needs all blocks first). With
 // KSMOOTH the keys are fp32(k - kbar) before their block amax and codes.
+// With VSMOOTH the block's V mean mu = bf16(fp32(sum / n)) per channel (sum in
+// float64 over the n valid tokens) is stored, and the V amax is that of the
+// residuals fp32(v - mu).
 // grid (nQB, H, B), 256 threads; thread -> rows {32p + tid/8}, channels 16*(tid%8)..+16
-template <bool FP16, bool KSMOOTH>
+template <bool FP16, bool KSMOOTH, bool VSMOOTH>
 __global__ __launch_bounds__(256) void prep_qk_kernel(PrepArgs a) {
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, rsub = tid >> 3, oc = tid & 7;
@@ -149,7 +152,7 @@ __global__ __launch_bounds__(256) void prep_qk_kernel(PrepArgs a) {
   const bool kv = blk < a.nT;
   __shared__ float red[16];
 
-  uint4 ql[4], qh[4], kl[4], kh[4];
+  uint4 ql[4], qh[4], kl[4], kh[4], vl[4], vh[4];
   uint32_t mq = 0, mk = 0, mv = 0;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
@@ -160,9 +163,51 @@ __global__ __launch_bounds__(256) void prep_qk_kernel(PrepArgs a) {
     mq = absmax_bits(ql[p], qh[p], mq);
     load16(a.k + off, valid && kv, kl[p], kh[p]);
     mk = absmax_bits(kl[p], kh[p], mk);
-    uint4 vl, vh;
-    load16(a.v + off, valid && kv, vl, vh);
-    mv = absmax_bits(vl, vh, mv);
+    load16(a.v + off, valid && kv, vl[p], vh[p]);
+    mv = absmax_bits(vl[p], vh[p], mv);
+  }
+  float amv_local = bits_to_f32<FP16>(mv);
+  if (VSMOOTH && kv) {
+    // block mean per channel: per-thread sums of its 4 rows (padding rows are
+    // zero), then the 32 row groups in order
+    __shared__ double vsum[32][HEAD_DIM + 1];
+    __shared__ float vmu_s[HEAD_DIM];
+    double acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.0;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t w[8] = {vl[p].x, vl[p].y, vl[p].z, vl[p].w, vh[p].x, vh[p].y, vh[p].z, vh[p].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        acc[2 * i] += (double)bits_to_f32<FP16>(w[i] & 0xFFFFu);
+        acc[2 * i + 1] += (double)bits_to_f32<FP16>(w[i] >> 16);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) vsum[rsub][16 * oc + i] = acc[i];
+    __syncthreads();
+    if (tid < HEAD_DIM) {
+      double t = 0.0;
+      for (int r = 0; r < 32; ++r) t += vsum[r][tid];
+      const int n = min(KTILE, a.S - blk * KTILE);
+      const uint32_t hb = f32_to_bf16((float)(t / (double)n));
+      vmu_s[tid] = bf16_to_f32(hb);
+      a.vmu[((int64_t)bh * a.nT + blk) * HEAD_DIM + tid] = (uint16_t)hb;
+    }
+    __syncthreads();
+    amv_local = 0.0f;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const bool valid = blk * KTILE + 32 * p + rsub < a.S;
+      const uint32_t w[8] = {vl[p].x, vl[p].y, vl[p].z, vl[p].w, vh[p].x, vh[p].y, vh[p].z, vh[p].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float r0 = bits_to_f32<FP16>(w[i] & 0xFFFFu) - vmu_s[16 * oc + 2 * i];
+        const float r1 = bits_to_f32<FP16>(w[i] >> 16) - vmu_s[16 * oc + 2 * i + 1];
+        if (valid) amv_local = __builtin_fmaxf(amv_local, __builtin_fmaxf(__builtin_fabsf(r0), __builtin_fabsf(r1)));
+      }
+    }
   }
   float ks[KSMOOTH ? 4 : 1][16];
   float amk_local = bits_to_f32<FP16>(mk);
@@ -187,7 +232,7 @@ __global__ __launch_bounds__(256) void prep_qk_kernel(PrepArgs a) {
   }
   const float amq = block_max(bits_to_f32<FP16>(mq), red);
   const float amk = block_max(amk_local, red + 4);
-  const float amv = block_max(bits_to_f32<FP16>(mv), red + 8);
+  const float amv = block_max(amv_local, red + 8);
   float sq, iq, sk, ik;
   quant_scales(amq, sq, iq);
   quant_scales(amk, sk, ik);
@@ -214,11 +259,26 @@ __global__ __launch_bounds__(256) void prep_qk_kernel(PrepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// 16 halves minus 16 per-channel fp32 offsets -> 16 E4M3 bytes of fp32(x - mu) * inv
+template <bool FP16>
+__device__ inline uint4 encode16_sub(uint4 lo, uint4 hi, const float (&mu)[16], float inv) {
+  const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[2 * i] = bits_to_f32<FP16>(w[i] & 0xFFFFu) - mu[2 * i];
+    x[2 * i + 1] = bits_to_f32<FP16>(w[i] >> 16) - mu[2 * i + 1];
+  }
+  return encode16f(x, inv);
+}
+
 // Kernel 2: per (b, h, key tile): head V scale from the block maxima, V codes
 // transposed and packed into the PV operand order (through LDS), and with
-// repair the residual energy of every token.
+// repair the residual energy of every token. With VSMOOTH the codes are of
+// fp32(v - mu) for the tile's block mean mu, and mu * inv is stored in the
+// attention kernel's lane order.
 // grid (nT, H, B), 256 threads; thread -> tokens 4m..4m+3 (m = tid/8), channels 16*(tid%8)..+16
-template <bool FP16, bool REPAIR>
+template <bool FP16, bool REPAIR, bool VSMOOTH>
 __global__ __launch_bounds__(256) void prep_v_kernel(PrepArgs a) {
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, m = tid >> 3, oc = tid & 7;
@@ -236,13 +296,26 @@ __global__ __launch_bounds__(256) void prep_v_kernel(PrepArgs a) {
     a.sv[2 * bh + 1] = inv;
   }
 
+  float mu[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c)
+    mu[c] = VSMOOTH ? bf16_to_f32(a.vmu[((int64_t)bh * a.nT + tile) * HEAD_DIM + 16 * oc + c]) : 0.0f;
+  if (VSMOOTH && m == 0) {
+    // mu * inv for channel d = 16n + 4g + r at lane-order slot 32g + 4n + r
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const int d = 16 * oc + c, n = d >> 4, g = (d >> 2) & 3, r = d & 3;
+      a.vmus[((int64_t)bh * a.nT + tile) * HEAD_DIM + 32 * g + 4 * n + r] = mu[c] * inv;
+    }
+  }
   uint4 lo[4], hi[4], cd[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int tok = tile * KTILE + 4 * m + r;
     const int64_t off = (int64_t)b * a.sb + (int64_t)tok * a.ss + (int64_t)h * a.sh + 16 * oc;
     load16(a.v + off, tok < a.S, lo[r], hi[r]);
-    cd[r] = encode16<FP16>(lo[r], hi[r], inv);
+    if (VSMOOTH) cd[r] = tok < a.S ? encode16_sub<FP16>(lo[r], hi[r], mu, inv) : make_uint4(0, 0, 0, 0);
+    else cd[r] = encode16<FP16>(lo[r], hi[r], inv);
   }
   // transpose: channel d = 16*oc + c gets the 4 bytes of tokens 4m..4m+3,
   // which sit in 4 consecutive columns of the packed tile
@@ -277,7 +350,7 @@ __global__ __launch_bounds__(256) void prep_v_kernel(PrepArgs a) {
       double e = 0.0;
 #pragma unroll
       for (int c = 0; c < 16; ++c) {
-        const float x = bits_to_f32<FP16>((w[c >> 1] >> (16 * (c & 1))) & 0xFFFFu);
+        const float x = __fsub_rn(bits_to_f32<FP16>((w[c >> 1] >> (16 * (c & 1))) & 0xFFFFu), mu[c]);
         const float t = __fmul_rn(sv, e4m3_decode((cw[c >> 2] >> (8 * (c & 3))) & 0xFFu));
         const double d = (double)__fsub_rn(x, t);
         e = __builtin_fma(d, d, e);
@@ -314,10 +387,16 @@ __device__ inline int block_exclusive_scan(int v, int* scratch, int& total) {
   return before + x - v;
 }
 
+// V-Smooth block mean of channel c for token tok (0 without smoothing)
+__device__ inline float vmean_of(const PrepArgs& a, int bh, int tok, int c) {
+  return a.vmu ? bf16_to_f32(a.vmu[((int64_t)bh * a.nT + (tok >> 7)) * HEAD_DIM + c]) : 0.0f;
+}
+
 // residual of one value element, recomputed exactly as prep_v_kernel does
+// (mu: the element's V-Smooth block mean, 0 without smoothing)
 template <bool FP16>
-__device__ inline float residual(uint32_t hbits, float sv, float inv) {
-  const float x = bits_to_f32<FP16>(hbits);
+__device__ inline float residual(uint32_t hbits, float mu, float sv, float inv) {
+  const float x = __fsub_rn(bits_to_f32<FP16>(hbits), mu);
   const uint32_t code = e4m3_encode2(x * inv, 0.0f) & 0xFFu;
   return __fsub_rn(x, __fmul_rn(sv, e4m3_decode(code)));
 }
@@ -400,7 +479,7 @@ __global__ __launch_bounds__(1024) void select_kernel(PrepArgs a) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const float r = residual<FP16>((ws[c >> 1] >> (16 * (c & 1))) & 0xFFFFu, sv, inv);
+      const float r = residual<FP16>((ws[c >> 1] >> (16 * (c & 1))) & 0xFFFFu, vmean_of(a, bh, tok, c8 + c), sv, inv);
       mx = __builtin_fmaxf(mx, __builtin_fabsf(r));
     }
   }
@@ -462,10 +541,11 @@ __global__ __launch_bounds__(256) void pack_repair_kernel(PrepArgs a) {
     const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float r0 = residual<FP16>(w[2 * q] & 0xFFFFu, sv, inv) * rinv;
-      const float r1 = residual<FP16>(w[2 * q] >> 16, sv, inv) * rinv;
-      const float r2 = residual<FP16>(w[2 * q + 1] & 0xFFFFu, sv, inv) * rinv;
-      const float r3 = residual<FP16>(w[2 * q + 1] >> 16, sv, inv) * rinv;
+      const int c0 = 16 * oc + 4 * q;
+      const float r0 = residual<FP16>(w[2 * q] & 0xFFFFu, vmean_of(a, bh, tok, c0), sv, inv) * rinv;
+      const float r1 = residual<FP16>(w[2 * q] >> 16, vmean_of(a, bh, tok, c0 + 1), sv, inv) * rinv;
+      const float r2 = residual<FP16>(w[2 * q + 1] & 0xFFFFu, vmean_of(a, bh, tok, c0 + 2), sv, inv) * rinv;
+      const float r3 = residual<FP16>(w[2 * q + 1] >> 16, vmean_of(a, bh, tok, c0 + 3), sv, inv) * rinv;
       cw[r][q] = e4m3_encode2(r0, r1) | (e4m3_encode2(r2, r3) << 16);
     }
   }
@@ -487,29 +567,34 @@ __global__ __launch_bounds__(256) void pack_repair_kernel(PrepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-template <bool FP16>
+template <bool FP16, bool VSMOOTH>
 static void launch_qk(const PrepArgs& a, hipStream_t st) {
   const dim3 g1(a.nQB, a.H, a.B), g2(a.nT, a.H, a.B);
   if (a.kmean != nullptr) {
     hipLaunchKernelGGL(kmean_partial_kernel<FP16>, g2, dim3(256), 0, st, a);
     hipLaunchKernelGGL(kmean_final_kernel, dim3(a.H, a.B), dim3(1024), 0, st, a);
-    hipLaunchKernelGGL((prep_qk_kernel<FP16, true>), g1, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prep_qk_kernel<FP16, true, VSMOOTH>), g1, dim3(256), 0, st, a);
   } else {
-    hipLaunchKernelGGL((prep_qk_kernel<FP16, false>), g1, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prep_qk_kernel<FP16, false, VSMOOTH>), g1, dim3(256), 0, st, a);
   }
 }
 
-hipError_t launch_prepare(const PrepArgs& a, bool fp16, hipStream_t st) {
+template <bool FP16, bool VSMOOTH>
+static void launch_qkv(const PrepArgs& a, hipStream_t st) {
   const dim3 g2(a.nT, a.H, a.B);
-  const bool rep = a.energy != nullptr;
+  launch_qk<FP16, VSMOOTH>(a, st);
+  if (a.energy != nullptr) hipLaunchKernelGGL((prep_v_kernel<FP16, true, VSMOOTH>), g2, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((prep_v_kernel<FP16, false, VSMOOTH>), g2, dim3(256), 0, st, a);
+}
+
+hipError_t launch_prepare(const PrepArgs& a, bool fp16, hipStream_t st) {
+  const bool rep = a.energy != nullptr, vs = a.vmu != nullptr;
   if (fp16) {
-    launch_qk<true>(a, st);
-    if (rep) hipLaunchKernelGGL((prep_v_kernel<true, true>), g2, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((prep_v_kernel<true, false>), g2, dim3(256), 0, st, a);
+    if (vs) launch_qkv<true, true>(a, st);
+    else launch_qkv<true, false>(a, st);
   } else {
-    launch_qk<false>(a, st);
-    if (rep) hipLaunchKernelGGL((prep_v_kernel<false, true>), g2, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((prep_v_kernel<false, false>), g2, dim3(256), 0, st, a);
+    if (vs) launch_qkv<false, true>(a, st);
+    else launch_qkv<false, false>(a, st);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !rep || a.n_sel == 0) return e;

@@ -121,11 +121,17 @@ typedef struct oc_attn_desc {
  *   sr     f32 [B][H][2]              {amax/448, 448/amax} of the selected residuals
  *   kmean  f32 [B][H][128]            mean key per channel (K-mean smoothing only)
  *   kpart  f64 [B][H][n_ktiles][128]  per-block key sums (K-mean smoothing only)
+ *   vmu    bf16 [B][H][n_ktiles][128] V block means (V-Smooth only; vpack then
+ *                                     holds the codes of v - mean, and sv and
+ *                                     vamax refer to those residuals)
+ *   vmus   f32 [B][H][n_ktiles][128]  mean * 448/amax in the attention kernel's
+ *                                     lane order: slot 32g + 4n + r holds channel
+ *                                     16n + 4g + r (V-Smooth only)
  */
 typedef struct oc_attn_ws_layout {
   uint64_t qhat, kpack, vpack, sq, sk, vamax, sv;
   uint64_t energy, sel, kselpack, rpack, sksel, sr;
-  uint64_t kmean, kpart;
+  uint64_t kmean, kpart, vmu, vmus;
   uint64_t total_bytes;
   int32_t n_ktiles, n_qtiles, s_pad_q, n_sel_max, n_sel_tiles_max;
 } oc_attn_ws_layout;
@@ -163,6 +169,17 @@ oc_status oc_attn_plan_set_weights(oc_attn_plan* plan, int weights);
  * write-up, section on why attention is the video bottleneck), so it is an
  * option. enable must be 0 or 1, else OC_ERR_INVALID_ARGUMENT. */
 oc_status oc_attn_plan_set_k_smoothing(oc_attn_plan* plan, int enable);
+/* V-Smooth block means for later prepare calls on this plan (host-only;
+ * default off; VC-Attention write-up, section "V-Smooth", without its k-means
+ * grouping of tokens). When on, each 128-token block of V loses its mean,
+ * mu = bf16(fp32(sum_j v_j / n)) per channel over the block's n tokens (sum in
+ * float64), and the per-head E4M3 quantization (and, with repair, the residual
+ * selection) acts on fp32(v - mu). The attention on such a workspace adds the
+ * means back with each key tile's row sum:
+ *   O_i = (sv * sum_j P_ij dec(r_j) + sum_t l_it mu_t) / L_i.
+ * oc_attn_forward_prepared follows the setting the workspace was prepared
+ * with. enable must be 0 or 1, else OC_ERR_INVALID_ARGUMENT. */
+oc_status oc_attn_plan_set_v_smoothing(oc_attn_plan* plan, int enable);
 /* Workspace bytes the plan needs (host-only). */
 oc_status oc_attn_workspace_size(const oc_attn_plan* plan, size_t* bytes);
 /* Buffer offsets inside the workspace (host-only). */

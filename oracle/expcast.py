@@ -41,6 +41,14 @@ Readings where the pages leave a step open (each is listed in the design doc):
     of its (batch, head), k' = fp32(k - kbar) with kbar = fp32(sum_j k_j / S)
     per channel. q.k' = q.k - q.kbar shifts each score row by a constant, which
     softmax ignores.
+  * V-Smooth block means (an option, off by default; VC-Attention write-up,
+    section "V-Smooth", without its k-means grouping): every 128-token block
+    of V loses its mean, mu_t = bf16(fp32(sum_j v_j / n_t)) per channel over
+    the block's n_t tokens (sum in float64); the residuals fp32(v - mu_t) are
+    quantized with the per-head scale in place of v; the output adds the means
+    back with each key tile's row sum: O_i = (sv * sum_j P_ij dec(r_j) +
+    sum_t l_it mu_t) / L_i, l_it = sum over tile t of P_ij. With repair, the
+    repaired residual is taken of fp32(v - mu_t) in place of v.
   * repair: residual r = v - sv*dec(v_hat) in fp32; energy = sum over the 128
     channels of r^2 accumulated in float64 in channel order; the top
     k = ceil(budget*S) tokens by energy (ties to the lower index) are repaired
@@ -117,6 +125,7 @@ class PreparedHead:
     vc: np.ndarray
     sv: np.float32
     repair: RepairSet | None = field(default=None)
+    vmean: np.ndarray | None = field(default=None)   # V-Smooth: [n_blocks, 128] block means (bf16 values)
 
     @property
     def S(self):
@@ -161,15 +170,43 @@ def smooth_keys(k: np.ndarray) -> np.ndarray:
     return (k.astype(F32) - key_mean(k)).astype(np.float64)
 
 
+def to_bf16(x: np.ndarray) -> np.ndarray:
+    """fp32 values -> nearest bf16 values (round to nearest even), as float64."""
+    u = np.asarray(x, dtype=F32).view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(F32).astype(np.float64)
+
+
+def value_block_means(v: np.ndarray, block: int = QK_BLOCK) -> np.ndarray:
+    """V-Smooth block means [n_blocks, 128]: bf16(fp32(sum / n)) over each
+    block's tokens, the sum in float64."""
+    S = v.shape[0]
+    n = (S + block - 1) // block
+    mu = np.empty((n, v.shape[1]))
+    for t in range(n):
+        blk = v[t * block:min(S, (t + 1) * block)]
+        mu[t] = to_bf16((blk.sum(axis=0) / blk.shape[0]).astype(F32))
+    return mu
+
+
+def smooth_values(v: np.ndarray, mu: np.ndarray, block: int = QK_BLOCK) -> np.ndarray:
+    """fp32(v - mu of the token's block), as float64."""
+    m = mu[np.arange(v.shape[0]) // block]
+    return (v.astype(F32) - m.astype(F32)).astype(np.float64)
+
+
 def prepare_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, budget: float = 0.0,
-                 k_smooth: bool = False) -> PreparedHead:
+                 k_smooth: bool = False, v_smooth: bool = False) -> PreparedHead:
     """Quantize one (batch, head) slice; inputs are float64 [S, 128] holding
-    bf16/fp16-exact values. k_smooth subtracts the mean key first."""
+    bf16/fp16-exact values. k_smooth subtracts the mean key first; v_smooth
+    quantizes V as block-mean residuals."""
     qc, sq = quantize_blocks(q)
     kc, sk = quantize_blocks(smooth_keys(k) if k_smooth else k)
-    vc, sv = quantize_head(v)
-    rep = repair_select(v, vc, sv, budget) if budget > 0 else None
-    return PreparedHead(qc, sq, kc, sk, vc, sv, rep)
+    mu = value_block_means(v) if v_smooth else None
+    vv = smooth_values(v, mu) if v_smooth else v
+    vc, sv = quantize_head(vv)
+    rep = repair_select(vv, vc, sv, budget) if budget > 0 else None
+    return PreparedHead(qc, sq, kc, sk, vc, sv, rep, mu)
 
 
 def log2_logits(ph: PreparedHead, rows, tau: float) -> np.ndarray:
@@ -212,7 +249,7 @@ def exp_cast_codes(x: np.ndarray, M) -> np.ndarray:
 
 
 def expcast_attention_head(q, k, v, tau=None, rows=None, budget=0.0, ph=None,
-                           quantize=True, weights="expcast", chunk=512, k_smooth=False):
+                           quantize=True, weights="expcast", chunk=512, k_smooth=False, v_smooth=False):
     """Output rows of ExpCast attention for one (batch, head) slice.
 
     q, k, v: float64 [S, 128]. Returns a dict with the float64 output rows
@@ -229,7 +266,7 @@ def expcast_attention_head(q, k, v, tau=None, rows=None, budget=0.0, ph=None,
     rows = np.arange(S) if rows is None else np.asarray(rows)
     if ph is None:
         if quantize:
-            ph = prepare_head(q, k, v, budget, k_smooth=k_smooth)
+            ph = prepare_head(q, k, v, budget, k_smooth=k_smooth, v_smooth=v_smooth)
         else:
             ones = lambda n: np.ones(n, dtype=F32)  # noqa: E731
             ph = PreparedHead(None, ones((S + QK_BLOCK - 1) // QK_BLOCK), None,
@@ -255,6 +292,8 @@ def expcast_attention_head(q, k, v, tau=None, rows=None, budget=0.0, ph=None,
             raise ValueError(weights)
         L = P.sum(axis=1)
         acc = float(ph.sv) * (P @ vd)
+        if quantize and ph.vmean is not None:
+            acc += P @ ph.vmean[np.arange(S) // QK_BLOCK]     # the block means, weighted by the row sums
         if quantize and ph.repair is not None and ph.repair.k > 0:
             rp = ph.repair
             acc += float(rp.sr) * (P[:, rp.sel] @ decode(rp.rc))
@@ -281,7 +320,7 @@ def key_tile_order(n_tiles: int) -> list:
 
 
 def expcast_attention_online(q, k, v, tau=None, rows=None, budget=0.0, ph=None, order="mid", chunk=256,
-                             m_trace=None, weights="expcast", k_smooth=False):
+                             m_trace=None, weights="expcast", k_smooth=False, v_smooth=False):
     """Single-pass (flash) form of ExpCast attention, as the pages' kernel runs
     it: keys are consumed in 128-key tiles in `order` ("mid" = key_tile_order,
     "ascending" = 0, 1, 2, ...). Per row, a running bit-aligned max M is raised
@@ -311,7 +350,7 @@ def expcast_attention_online(q, k, v, tau=None, rows=None, budget=0.0, ph=None, 
     tau = 1.0 / math.sqrt(D) if tau is None else tau
     rows = np.arange(S) if rows is None else np.asarray(rows)
     if ph is None:
-        ph = prepare_head(q, k, v, budget, k_smooth=k_smooth)
+        ph = prepare_head(q, k, v, budget, k_smooth=k_smooth, v_smooth=v_smooth)
     nT = (S + QK_BLOCK - 1) // QK_BLOCK
     tiles = key_tile_order(nT) if order == "mid" else list(range(nT))
     vd = decode(ph.vc)
@@ -324,6 +363,7 @@ def expcast_attention_online(q, k, v, tau=None, rows=None, budget=0.0, ph=None, 
         x = log2_logits(ph, r, tau)
         M = np.full(len(r), -np.inf)
         O = np.zeros((len(r), D))
+        Omu = np.zeros((len(r), D))        # V-Smooth: sum over tiles of (tile row sum) * (block mean)
         L = np.zeros(len(r))
         for t in tiles:
             ks = slice(t * QK_BLOCK, min(S, (t + 1) * QK_BLOCK))
@@ -335,10 +375,13 @@ def expcast_attention_online(q, k, v, tau=None, rows=None, budget=0.0, ph=None, 
             f = np.where(np.isinf(M), 0.0, np.exp2(M - Mn))     # exact powers of two
             P = VALUES[codes_of(xt, Mn)]
             O = O * f[:, None] + P @ vd[ks]
+            if ph.vmean is not None:
+                Omu = Omu * f[:, None] + P.sum(axis=1)[:, None] * ph.vmean[t][None, :]
             L = L * f + P.sum(axis=1)
             M = Mn
             trace[c0:c0 + len(r), t] = Mn.astype(np.int64)
         O *= float(ph.sv)
+        O += Omu
         if ph.repair is not None and ph.repair.k > 0:
             rp = ph.repair
             P = VALUES[codes_of(x[:, rp.sel], M)]

@@ -118,6 +118,14 @@ class WsView:
     def sr(self, b, h):
         return self._arr(self.L.sr + 8 * self.bh(b, h), np.float32, 2)
 
+    def vmu(self, b, h):
+        n = self.L.n_ktiles * 128
+        return self._arr(self.L.vmu + 2 * n * self.bh(b, h), np.uint16, n).reshape(self.L.n_ktiles, 128)
+
+    def vmus(self, b, h):
+        n = self.L.n_ktiles * 128
+        return self._arr(self.L.vmus + 4 * n * self.bh(b, h), np.float32, n).reshape(self.L.n_ktiles, 128)
+
     def kmean(self, b, h):
         return self._arr(self.L.kmean + 4 * 128 * self.bh(b, h), np.float32, 128)
 
@@ -126,14 +134,14 @@ class WsView:
 
 
 def oracle_rows(q, k, v, b, h, rows, budget=0.0, tau=None, order="mid", m_trace=None, weights="expcast",
-                k_smooth=False):
+                k_smooth=False, v_smooth=False):
     """oracle output rows for one (b, h), in the single-pass form the kernel
     computes (key tiles from the middle of the window outwards), plus the
     prepared head; m_trace replays given running-max decisions; weights
     "exp_cast" is the comparison byte path"""
     qh, kh, vh = head64(q, b, h), head64(k, b, h), head64(v, b, h)
     return oracle.expcast_attention_online(qh, kh, vh, tau=tau, rows=rows, budget=budget, order=order,
-                                           m_trace=m_trace, weights=weights, k_smooth=k_smooth)
+                                           m_trace=m_trace, weights=weights, k_smooth=k_smooth, v_smooth=v_smooth)
 
 
 def out_rows(out, b, h, rows):

@@ -187,3 +187,20 @@ def test_k_smoothing_buffers_in_layout():
         assert L.total_bytes >= L.kpart + 2 * 3 * nT * 128 * 8
     finally:
         lib.oc_attn_plan_destroy(p)
+
+
+def test_set_v_smoothing_accepts_0_and_1():
+    st, p = create(make_desc())
+    assert st == oc.OC_OK
+    try:
+        assert lib.oc_attn_plan_set_v_smoothing(p, 1) == oc.OC_OK
+        assert lib.oc_attn_plan_set_v_smoothing(p, 0) == oc.OC_OK
+        for bad in (-1, 2):
+            assert lib.oc_attn_plan_set_v_smoothing(p, bad) == oc.OC_ERR_INVALID_ARGUMENT
+        assert lib.oc_attn_plan_set_v_smoothing(None, 0) == oc.OC_ERR_INVALID_ARGUMENT
+        L = oc.WsLayout()
+        assert lib.oc_attn_workspace_layout(p, ctypes.byref(L)) == oc.OC_OK
+        nT = math.ceil(1000 / 128)
+        assert L.vmus >= L.vmu + 4 * nT * 128 * 2 and L.total_bytes >= L.vmus + 4 * nT * 128 * 4
+    finally:
+        lib.oc_attn_plan_destroy(p)

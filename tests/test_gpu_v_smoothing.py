@@ -1,0 +1,144 @@
+"""V-Smooth block means against the oracle: the bf16 block means, the
+residual codes and scale, the scaled means in the kernel's lane order and,
+with repair, the residual energies and selection, bit-exact; attention with the
+means added back per key tile within 5e-3 of the oracle; lower error than the
+plain path on values with a per-channel bias."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import WsView, head64, log, out_rows
+from test_gpu_attention import _compare
+
+pytestmark = pytest.mark.gpu
+
+
+def _oc():
+    import bit_fp8_attention_block_amd as oc
+    return oc
+
+
+def _biased_values(B, S, H, seed, dtype=torch.bfloat16):
+    """q, k ~ N(0,1); v ~ N(0,1) plus an N(0, 5^2) bias per (head, channel)."""
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, S, H, 128, generator=g)
+    k = torch.randn(B, S, H, 128, generator=g)
+    v = torch.randn(B, S, H, 128, generator=g) + 5.0 * torch.randn(1, 1, H, 128, generator=g)
+    return tuple(t.to(dtype).cuda() for t in (q, k, v))
+
+
+def _lane_order(mu_scaled):
+    """[n, 128] per channel -> slot 32g + 4n + r holds channel 16n + 4g + r"""
+    out = np.empty_like(mu_scaled)
+    for d in range(128):
+        n, g, r = d >> 4, (d >> 2) & 3, d & 3
+        out[:, 32 * g + 4 * n + r] = mu_scaled[:, d]
+    return out
+
+
+@pytest.mark.parametrize("case", ["s1024_h2", "ragged_fp16", "biased", "repair"])
+def test_smoothed_value_prepare_bit_exact(case):
+    oc = _oc()
+    log(f"[v-smooth prepare] case={case}")
+    budget = None
+    if case == "s1024_h2":
+        q, k, v = workloads.make_inputs("s1024_h2", device="cuda")
+    elif case == "ragged_fp16":
+        q, k, v = workloads.make_inputs("b2_s70000_h40_fp16", device="cuda", S=300, H=3)
+    elif case == "biased":
+        q, k, v = _biased_values(1, 700, 2, seed=4)
+    else:
+        q, k, v = workloads.make_inputs("s8192_h8", device="cuda", S=1500, H=2)
+        budget = 0.02
+    prep = oc.prepare(q, k, v, budget=budget, v_smooth=True)
+    torch.cuda.synchronize()
+    w = WsView(prep)
+    B, S, H, _ = q.shape
+    for b in range(B):
+        for h in range(H):
+            vh = head64(v, b, h)
+            ph = oracle.prepare_head(head64(q, b, h), head64(k, b, h), vh, budget=budget or 0.0, v_smooth=True)
+            mu_bits = (ph.vmean.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+            assert np.array_equal(w.vmu(b, h), mu_bits), (b, h, "block means")
+            assert np.array_equal(w.vcodes(b, h), ph.vc), (b, h, "residual codes")
+            s, inv = w.sv(b, h)
+            assert s == ph.sv, (b, h, "residual scale")
+            want = _lane_order(ph.vmean.astype(np.float32) * np.float32(inv))
+            assert np.array_equal(w.vmus(b, h), want), (b, h, "scaled means")
+            if budget:
+                rp = ph.repair
+                assert np.array_equal(w.energy(b, h), rp.energy) or np.allclose(w.energy(b, h), rp.energy,
+                                                                                  rtol=1e-14, atol=0)
+                assert np.array_equal(w.sel(b, h, rp.k), rp.sel), (b, h, "selection")
+                assert np.array_equal(w.rcodes(b, h, rp.k), rp.rc), (b, h, "repair codes")
+                assert w.sr(b, h)[0] == rp.sr
+
+
+@pytest.mark.parametrize("name", ["s8192_h8", "biased"])
+def test_smoothed_value_attention_matches_oracle(name):
+    oc = _oc()
+    log(f"[v-smooth attention] {name}")
+    if name == "biased":
+        q, k, v = _biased_values(1, 4000, 2, seed=5)
+        rows, pairs = np.arange(0, 4000, 9), [(0, 0), (0, 1)]
+    else:
+        q, k, v = workloads.make_inputs(name, device="cuda")
+        rows, pairs = np.array(workloads.sample_rows(8192, 256, seed=2)), [(0, 0), (0, 6)]
+    out = oc.attention(q, k, v, v_smooth=True)
+    prep = oc.prepare(q, k, v, v_smooth=True)
+    torch.cuda.synchronize()
+    _compare(q, k, v, out, pairs, rows, label=name + " V-Smooth", prep=prep, v_smooth=True)
+
+
+def test_smoothed_value_attention_with_repair_matches_oracle():
+    oc = _oc()
+    q, k, v = _biased_values(1, 2000, 2, seed=6)
+    out = oc.attention_v_repair(q, k, v, 0.01, v_smooth=True)
+    prep = oc.prepare_v_repair(q, k, v, 0.01, v_smooth=True)
+    torch.cuda.synchronize()
+    _compare(q, k, v, out, [(0, 0), (0, 1)], np.arange(0, 2000, 3), budget=0.01, label="V-Smooth + repair",
+             prep=prep, v_smooth=True)
+
+
+def test_smoothing_lowers_value_error_on_channel_biased_values():
+    """The values the kernel multiplies by (block mean + sv * residual code,
+    read back from the workspace) against the input values: removing a
+    per-channel bias shrinks the E4M3 range, so the error drops sharply. The
+    attention output improves too, down to the BF16 output rounding."""
+    oc = _oc()
+    q, k, v = _biased_values(1, 4096, 2, seed=7)
+    prep_s = oc.prepare(q, k, v, v_smooth=True)
+    prep_p = oc.prepare(q, k, v)
+    plain = oc.attention(q, k, v)
+    smooth = oc.attention(q, k, v, v_smooth=True)
+    torch.cuda.synchronize()
+    ws, wp = WsView(prep_s), WsView(prep_p)
+    rows = np.arange(0, 4096, 16)
+    for h in range(2):
+        vh = head64(v, 0, h)
+        rec_p = float(wp.sv(0, h)[0]) * oracle.decode(wp.vcodes(0, h))
+        mu = (ws.vmu(0, h).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        rec_s = mu[np.arange(4096) // 128] + float(ws.sv(0, h)[0]) * oracle.decode(ws.vcodes(0, h))
+        ev0, ev1 = oracle.rel_l2(rec_p, vh), oracle.rel_l2(rec_s, vh)
+        exact = oracle.exact_attention_head(head64(q, 0, h), head64(k, 0, h), vh, rows=rows)
+        e0 = oracle.rel_l2(out_rows(plain, 0, h, rows), exact)
+        e1 = oracle.rel_l2(out_rows(smooth, 0, h, rows), exact)
+        log(f"  (h={h}) value rel-L2: plain {ev0:.5f}, V-Smooth {ev1:.5f}; "
+            f"output vs exact: plain {e0:.5f}, V-Smooth {e1:.5f}")
+        assert ev1 < 0.5 * ev0
+        assert e1 < e0
+
+
+def test_prepared_call_follows_the_workspace_setting():
+    oc = _oc()
+    q, k, v = workloads.make_inputs("s1024_h2", device="cuda")
+    full = oc.attention(q, k, v, v_smooth=True)
+    prep = oc.prepare(q, k, v, v_smooth=True)
+    other = oc.prepare(q, k, v)                       # same plan, smoothing off again
+    a = oc.attention_prepared(prep)
+    b = oc.attention_prepared(other)
+    plain = oc.attention(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(a, full) and torch.equal(b, plain) and not torch.equal(a, b)

@@ -2,6 +2,7 @@
 inputs, closed-form special cases, and the reduction to textbook softmax
 attention (checked against torch's SDPA in float64 on the CPU)."""
 import math
+import struct
 
 import numpy as np
 import pytest
@@ -40,14 +41,30 @@ def _scales(amax):
     return np.float32(a / np.float32(448)), np.float32(np.float32(448) / a)
 
 
-def brute_force(q, k, v, tau=TAU, k_smooth=False):
+def _bf16(x):
+    """fp32 value -> nearest bf16 value, ties to even, by its bit pattern"""
+    u = struct.unpack("<I", struct.pack("<f", float(np.float32(x))))[0]
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return struct.unpack("<f", struct.pack("<I", u & 0xFFFFFFFF))[0]
+
+
+def brute_force(q, k, v, tau=TAU, k_smooth=False, v_smooth=False):
     """ExpCast attention with explicit loops over tokens, channels and keys.
     k_smooth: subtract the mean key (exact sum by math.fsum, divided by S,
-    rounded to fp32; fp32 subtraction) before the K blocks are quantized."""
+    rounded to fp32; fp32 subtraction) before the K blocks are quantized.
+    v_smooth: quantize each value minus its 128-token block mean (bf16 of the
+    fp32 mean) and add the means back weighted by each block's weight sum."""
     S, D = len(k), len(k[0])
     if k_smooth:
         kbar = [np.float32(math.fsum(k[i][c] for i in range(S)) / S) for c in range(D)]
         k = [[float(np.float32(k[i][c]) - kbar[c]) for c in range(D)] for i in range(S)]
+    mu = None
+    if v_smooth:
+        mu = []
+        for b0 in range(0, S, 128):
+            blk = range(b0, min(S, b0 + 128))
+            mu.append([_bf16(math.fsum(v[i][c] for i in blk) / len(blk)) for c in range(D)])
+        v = [[float(np.float32(v[i][c]) - np.float32(mu[i // 128][c])) for c in range(D)] for i in range(S)]
     qc, kc, sq, sk = [None] * S, [None] * S, [0.0] * S, [0.0] * S
     for x, codes, sc in ((q, qc, sq), (k, kc, sk)):
         for b0 in range(0, S, 128):
@@ -67,7 +84,12 @@ def brute_force(q, k, v, tau=TAU, k_smooth=False):
         M = math.ceil(max(xs))
         w = [_dec(min(126, max(0, round(8 * (xj - M) + 120 - 0.35)))) for xj in xs]
         L = sum(w)
-        out.append([sum(w[j] * vd[j][c] for j in range(S)) / L for c in range(D)])
+        row = [sum(w[j] * vd[j][c] for j in range(S)) for c in range(D)]
+        if mu is not None:
+            for t in range(len(mu)):
+                lt = sum(w[j] for j in range(128 * t, min(S, 128 * t + 128)))
+                row = [row[c] + lt * mu[t][c] for c in range(D)]
+        out.append([x / L for x in row])
         Ms.append(M)
         Ls.append(L)
     return np.array(out), np.array(Ms), np.array(Ls)
@@ -250,6 +272,63 @@ def test_k_smoothing_brute_force_matches_vectorized(S):
     want = brute_force(q.tolist(), k.tolist(), v.tolist(), k_smooth=True)[0][rows]
     got = oracle.expcast_attention_head(q, k, v, rows=rows, k_smooth=True)["out"]
     np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("S", [2, 130])
+def test_v_smoothing_brute_force_matches_vectorized(S):
+    q, k, v = (t[0, :, 0].double().numpy() for t in workloads.random_qkv(1, S, 1, seed=S + 13, scale=2.0))
+    v = torch.from_numpy(v + 4.0 * np.cos(np.arange(128))[None, :]).bfloat16().double().numpy()
+    rows = [0, S - 1]
+    want = brute_force(q.tolist(), k.tolist(), v.tolist(), v_smooth=True)[0][rows]
+    got = oracle.expcast_attention_head(q, k, v, rows=rows, v_smooth=True)["out"]
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+    online = oracle.expcast_attention_online(q, k, v, rows=rows, v_smooth=True)["out"]
+    np.testing.assert_allclose(online, want, rtol=1e-9, atol=1e-10)
+
+
+def test_v_smoothing_is_exact_for_blockwise_constant_values():
+    """When every token of a block has the same value vector, the block mean
+    is that vector and the residuals are zero, so the value path is exact:
+    the output is the ExpCast weights applied to the unquantized values."""
+    rng = np.random.default_rng(8)
+    S = 300
+    blocks = rng.integers(-40, 40, size=(3, 128)) / 8.0          # bf16-exact
+    v = blocks[np.arange(S) // 128]
+    q = torch.from_numpy(rng.normal(size=(S, 128))).bfloat16().double().numpy()
+    k = torch.from_numpy(rng.normal(size=(S, 128))).bfloat16().double().numpy()
+    rows = np.arange(0, S, 7)
+    r = oracle.expcast_attention_head(q, k, v, rows=rows, v_smooth=True)
+    x = oracle.log2_logits(r["ph"], rows, TAU)
+    P = oracle.VALUES[oracle.expcast_codes(x, oracle.bitaligned_row_max(x))]
+    np.testing.assert_allclose(r["out"], (P @ v) / P.sum(axis=1, keepdims=True), rtol=1e-13, atol=1e-13)
+    plain = oracle.expcast_attention_head(q, k, v, rows=rows)["out"]
+    assert np.abs(plain - r["out"]).max() > 1e-3       # the plain path rounds V to E4M3
+
+
+def test_v_smoothing_lowers_error_on_channel_biased_values():
+    rng = np.random.default_rng(9)
+    S = 1024
+    q, k = rng.normal(size=(S, 128)), rng.normal(size=(S, 128))
+    v = rng.normal(size=(S, 128)) + rng.normal(0, 5, size=128)
+    q, k, v = (torch.from_numpy(t).bfloat16().double().numpy() for t in (q, k, v))
+    rows = np.arange(0, S, 4)
+    exact = oracle.exact_attention_head(q, k, v, rows=rows)
+    plain = oracle.rel_l2(oracle.expcast_attention_head(q, k, v, rows=rows)["out"], exact)
+    smooth = oracle.rel_l2(oracle.expcast_attention_head(q, k, v, rows=rows, v_smooth=True)["out"], exact)
+    assert smooth < 0.8 * plain, (plain, smooth)
+
+
+def test_v_smoothing_with_full_repair_restores_the_values():
+    """Budget 1 repairs every residual: the value path error falls to the
+    second-order quantization of the residual of the residual."""
+    q, k, v = (t[0, :, 0].double().numpy() for t in workloads.random_qkv(1, 256, 1, seed=21, scale=2.0))
+    rows = np.arange(0, 256, 5)
+    ph = oracle.prepare_head(q, k, v, budget=1.0, v_smooth=True)
+    x = oracle.log2_logits(ph, rows, TAU)
+    P = oracle.VALUES[oracle.expcast_codes(x, oracle.bitaligned_row_max(x))]
+    ideal = (P @ v) / P.sum(axis=1, keepdims=True)
+    got = oracle.expcast_attention_head(q, k, v, rows=rows, ph=ph)["out"]
+    assert oracle.rel_l2(got, ideal) < 2e-3
 
 
 def test_k_smoothing_removes_a_shared_key_offset_exactly():
