@@ -40,7 +40,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 # rocprofv3 PMC counters (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors a
 # plain 4 GiB copy gives; profiles/attn_kernel_s73397_h56.md). They are only
 # reported while the kernel sources still hash to the measured version.
-MEASURED_TRAFFIC = {"sources_sha256": "099ab3591a753edcd6bf1715a923efb5d842ccede358d38e9645cdd4e8a3fa08", "bytes": 11964233301}
+MEASURED_TRAFFIC = {"sources_sha256": "b2e1f8f26202df0609e516ef519bbcd95cdb4145c43bc7c94772b7747c0a592b", "bytes": 11964975456}
 KERNEL_SOURCES = ("bit_fp8_attention_block_amd/csrc/attention.hip", "bit_fp8_attention_block_amd/csrc/oc_common.h")
 
 
