@@ -131,6 +131,7 @@ class Plan:
         self.desc = Desc(B, S, H, 128, dt, strides[0], strides[1], strides[2], float(softmax_scale or 0.0))
         self.max_budget = float(max_budget)
         self._p = ctypes.c_void_p()
+        self._lib = _lib   # the library that owns the plan also destroys it
         _check(_lib.oc_attn_plan_create(ctypes.byref(self.desc), ctypes.c_double(self.max_budget),
                                         ctypes.byref(self._p)), "oc_attn_plan_create")
         n = ctypes.c_size_t()
@@ -140,9 +141,9 @@ class Plan:
         _check(_lib.oc_attn_workspace_layout(self._p, ctypes.byref(self.layout)), "oc_attn_workspace_layout")
 
     def __del__(self):
-        p = getattr(self, "_p", None)
-        if p is not None and p.value:
-            _lib.oc_attn_plan_destroy(p)
+        p, lib = getattr(self, "_p", None), getattr(self, "_lib", None)
+        if p is not None and p.value and lib is not None:
+            lib.oc_attn_plan_destroy(p)
             self._p = None
 
     @property

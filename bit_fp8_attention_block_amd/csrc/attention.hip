@@ -81,25 +81,31 @@ __device__ inline int tile_at(int s, int c, int nT, int order) {
 
 // One 16 KiB tile from global memory into LDS by direct global->LDS loads:
 // 1024 chunks of 16 bytes; each instruction moves 1 KiB per wave, lane l's
-// chunk landing at wave base + 16*l (the base is taken from M0).
+// chunk landing at wave base + 16*l (the base is taken from M0). Threads
+// 0..NT-1 take part; chunk i*NT + t of the tile is thread t's i-th.
+// The global address is a scalar base (tile + i*NT*16) plus the per-lane
+// offset voff = 16*t, and the LDS address is a scalar offset, so issuing a
+// tile costs no vector instructions.
 // Written as inline assembly so that the compiler does not track these loads:
 // it would otherwise drain all of them (vmcnt(0)) before every LDS read and
 // at every barrier, which rules out keeping a tile load in flight across an
 // iteration. The caller orders them with explicit vmcnt waits and
 // lds_barrier(). The s_nop covers the M0-write -> LDS-DMA hazard.
 template <int NT>
-__device__ inline void load_tile(uint8_t* lds_dst, const uint8_t* src) {
-  const int tid = threadIdx.x, wv = tid >> 6;
+__device__ inline void load_tile(uint32_t lds_dst, const uint8_t* src, uint32_t voff, int wv) {
 #pragma unroll
   for (int i = 0; i < 1024 / NT; ++i) {
-    const int ci = i * NT + tid;
-    const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(
-        lds_dst + (i * NT + wv * 64) * 16);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+    const uint32_t m0 = lds_dst + (uint32_t)(i * NT + wv * 64) * 16u;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
-                 : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src + ci * 16)
+                 : "s"(m0), "v"(voff), "s"(src + i * NT * 16)
                  : "memory", "m0");
   }
+}
+
+// byte offset in the workgroup's LDS of a pointer into it
+__device__ inline uint32_t lds_offset(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
 
 // Workgroup barrier that orders LDS accesses only (a full __syncthreads
@@ -131,12 +137,12 @@ constexpr int MU_SLOT = 1024;
 constexpr int LDS_BYTES_VS = LDS_BYTES + NBUF * MU_SLOT;
 
 // The 512 bytes of one tile's scaled block means into a 1 KiB LDS slot by one
-// wave's direct load (lanes 32-63 repeat lanes 0-31 into the upper half).
-__device__ inline void load_means(uint8_t* lds_dst, const uint8_t* src, int lane) {
-  const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_dst;
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+// wave's direct load (voff = 16*(lane%32): lanes 32-63 repeat lanes 0-31 into
+// the upper half).
+__device__ inline void load_means(uint32_t lds_dst, const uint8_t* src, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
-               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src + (lane & 31) * 16)
+               : "s"(lds_dst), "v"(voff), "s"(src)
                : "memory", "m0");
 }
 
@@ -378,7 +384,12 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   }
   const int bh = b * a.H + h;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
-  const bool group_b = a.grouping ? (wv & 1) != 0 : (wv >> 2) != 0;
+  const bool group_b = wv >= NWAVES / 2;
+  const int wvs = __builtin_amdgcn_readfirstlane(wv);
+  // LDS offsets of the K, V and block-mean buffers, and the per-lane offsets
+  // of the direct loads
+  const uint32_t kofs = lds_offset(kbuf), vofs = lds_offset(vbuf), mofs = lds_offset(mubuf);
+  const uint32_t voff = 16u * tid, voff_mu = 16u * (lane & 31);
   const int q0 = qt * BQ + wv * QBW * 16;
   const int qrow0 = q0 + l16;
   const int nT = a.nT;
@@ -421,17 +432,17 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   // prologue: K tiles 0..2 and V tiles 0..1
 #pragma unroll
   for (int i = 0; i < 3; ++i)
-    if (i < nT) load_tile<NTHREADS>(kbuf + i * TILE_BYTES, kt_ptr(i));
+    if (i < nT) load_tile<NTHREADS>(kofs + i * TILE_BYTES, kt_ptr(i), voff, wvs);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
-    if (i < nT) load_tile<NTHREADS>(vbuf + i * TILE_BYTES, vt_ptr(i));
+    if (i < nT) load_tile<NTHREADS>(vofs + i * TILE_BYTES, vt_ptr(i), voff, wvs);
   const auto mu_ptr = [&](int step) {
     return reinterpret_cast<const uint8_t*>(a.vmus + ((int64_t)bh * nT + tile_at(step, centre, nT, a.order)) * HEAD_DIM);
   };
   if (VSMOOTH && wv == 0) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      if (i < nT) load_means(mubuf + i * MU_SLOT, mu_ptr(i), lane);
+      if (i < nT) load_means(mofs + i * MU_SLOT, mu_ptr(i), voff_mu);
   }
   __builtin_amdgcn_s_waitcnt(0);   // this wave's chunks are in LDS
   __syncthreads();
@@ -441,10 +452,11 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
     const int j = tile_at(s, centre, nT, a.order);
     const int b0 = s & (NBUF - 1), b1 = (s + 1) & (NBUF - 1), bm1 = (s - 1) & (NBUF - 1);
     const bool ld_k = s + 3 < nT, ld_v = s + 2 < nT;
-    if (ld_k && !group_b) load_tile<NTHREADS / 2>(kbuf + ((s + 3) & (NBUF - 1)) * TILE_BYTES, kt_ptr(s + 3));
-    if (ld_v && !group_b) load_tile<NTHREADS / 2>(vbuf + ((s + 2) & (NBUF - 1)) * TILE_BYTES, vt_ptr(s + 2));
+    // (group A is waves 0-3, threads 0-255)
+    if (ld_k && !group_b) load_tile<NTHREADS / 2>(kofs + ((s + 3) & (NBUF - 1)) * TILE_BYTES, kt_ptr(s + 3), voff, wvs);
+    if (ld_v && !group_b) load_tile<NTHREADS / 2>(vofs + ((s + 2) & (NBUF - 1)) * TILE_BYTES, vt_ptr(s + 2), voff, wvs);
     const bool ld_mu = VSMOOTH && ld_v && wv == 0;
-    if (ld_mu) load_means(mubuf + ((s + 2) & (NBUF - 1)) * MU_SLOT, mu_ptr(s + 2), lane);
+    if (ld_mu) load_means(mofs + ((s + 2) & (NBUF - 1)) * MU_SLOT, mu_ptr(s + 2), voff_mu);
     const float skj = skp[j];
     if (!group_b) {
       expcast_tile<DUMP, EXPP>(S, P, aq, skj, M, O, L, j, j == last_masked, a, g, qrow0);
@@ -495,8 +507,8 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
     const float* sks = a.sksel + (int64_t)bh * nslot;
     for (int ts = 0; ts < a.n_sel_tiles; ++ts) {
       __syncthreads();   // every wave is done with the buffers about to be overwritten
-      load_tile<NTHREADS>(kbuf, ksb + (int64_t)ts * TILE_BYTES);
-      load_tile<NTHREADS>(vbuf, rsb + (int64_t)ts * TILE_BYTES);
+      load_tile<NTHREADS>(kofs, ksb + (int64_t)ts * TILE_BYTES, voff, wvs);
+      load_tile<NTHREADS>(vofs, rsb + (int64_t)ts * TILE_BYTES, voff, wvs);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
 #pragma unroll

@@ -47,7 +47,6 @@ struct oc_attn_plan {
   int n_sel_max;
   oc_attn_ws_layout L;
   int order;
-  int grouping;
   int exp_path;          // oc_weights: 0 ExpCast, 1 exp + FP8 cast
   int k_smooth;          // K-mean smoothing in prepare
   int v_smooth;          // V-Smooth block means (prepare and attention)
@@ -248,7 +247,6 @@ static AttnArgs attn_args(const oc_attn_plan* p, const void* ws, void* out, int 
   a.s_pad_q = L.s_pad_q;
   a.c8 = (float)(8.0 * (double)p->tau * 1.4426950408889634);
   a.order = p->order;
-  a.grouping = p->grouping;
   a.exp_path = p->exp_path;
   a.vmus = p->prepared_vsmooth(ws) ? (const float*)(base + L.vmus) : nullptr;
   return a;
@@ -337,8 +335,6 @@ oc_status oc_attn_plan_create(const oc_attn_desc* desc, double max_repair_budget
   p->n_sel_max = repair_count(max_repair_budget, d.S);
   const char* order = std::getenv("OC_ATTN_ORDER");
   p->order = (order && std::atoi(order) == 1) ? 1 : 0;
-  const char* grouping = std::getenv("OC_ATTN_GROUPING");
-  p->grouping = (grouping && std::atoi(grouping) == 1) ? 1 : 0;
   compute_layout(p);
   *plan = p;
   return OC_OK;

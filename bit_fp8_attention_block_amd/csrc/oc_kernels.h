@@ -53,7 +53,6 @@ struct AttnArgs {
   int B, S, H, nT, nQT, nQB, s_pad_q;
   float c8;                    // 8 * tau * log2(e)
   int order;                   // 0: from the middle of the key window outwards, 1: ascending
-  int grouping;                // which waves pair up on a SIMD: 0 = w and w+4, 1 = 2i and 2i+1
   int exp_path;                // 0: ExpCast bytes; 1: exp2 + FP32->E4M3 cast (comparison path)
   const float* vmus;           // V-Smooth: [B][H][nT][128] scaled block means (nullptr: off)
   uint8_t* dump_codes;         // debug: [S][S] bytes for one (b, h)
