@@ -149,41 +149,46 @@ __device__ inline void load_means(uint32_t lds_dst, const uint8_t* src, uint32_t
 // scheduling-group masks of __builtin_amdgcn_sched_group_barrier
 constexpr int SG_MFMA = 0x008, SG_VALU = 0x002, SG_DS_READ = 0x100;
 
-// S^T = K Q^T for one 128-key tile and the wave's 32 queries. The operand of
-// 16-key block kb+2 is read from LDS while the MFMAs of block kb run, so the
-// LDS latency hides behind 4 MFMAs instead of stalling every pair.
+// LDS operand read-ahead of the tile loops, in 16-row blocks: the operand of
+// block kb+RA is read while the MFMAs of block kb run
+constexpr int RA = 2;
+
+// S^T = K Q^T for one 128-key tile and the wave's 32 queries, with the K
+// operands read RA blocks ahead, so the LDS latency hides behind 2*RA MFMAs
+// instead of stalling every pair.
 __device__ __forceinline__ void qk_tile(const uint8_t* kt, const v8i (&qop)[QBW], v4f (&S)[QBW][8], int lane) {
   v8i kop[8];
-  kop[0] = lds_operand(kt, 0, lane);
-  kop[1] = lds_operand(kt, 1, lane);
+#pragma unroll
+  for (int kb = 0; kb < RA; ++kb) kop[kb] = lds_operand(kt, kb, lane);
 #pragma unroll
   for (int kb = 0; kb < 8; ++kb) {
-    if (kb + 2 < 8) kop[kb + 2] = lds_operand(kt, kb + 2, lane);
+    if (kb + RA < 8) kop[kb + RA] = lds_operand(kt, kb + RA, lane);
 #pragma unroll
     for (int qb = 0; qb < QBW; ++qb) S[qb][kb] = mfma_f8(kop[kb], qop[qb], v4f{0.f, 0.f, 0.f, 0.f});
   }
-  __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
+  __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2 * RA, 0);
 #pragma unroll
-  for (int kb = 0; kb < 6; ++kb) {
+  for (int kb = 0; kb < 8 - RA; ++kb) {
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, QBW, 0);
     __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2 * QBW, 0);
+  __builtin_amdgcn_sched_group_barrier(SG_MFMA, RA * QBW, 0);
 }
 
-// O^T += V^T P^T and (ROWSUM) L += 1 * P^T for one tile, with the same read-ahead
-template <bool ROWSUM = true>
+// O^T += V^T P^T and (ROWSUM) L += 1 * P^T for one tile, with the same
+// read-ahead. With PRE the first RA operands were read by the caller (pre).
+template <bool ROWSUM = true, bool PRE = false>
 __device__ __forceinline__ void pv_tile(const uint8_t* vt, const v8i (&P)[QBW], v4f (&O)[QBW][8], v4f (&L)[QBW],
-                                        int lane) {
+                                        int lane, const v8i* pre = nullptr) {
   v8i ones;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = 0x38383838;   // E4M3 1.0
   v8i vop[8];
-  vop[0] = lds_operand(vt, 0, lane);
-  vop[1] = lds_operand(vt, 1, lane);
+#pragma unroll
+  for (int n = 0; n < RA; ++n) vop[n] = PRE ? pre[n] : lds_operand(vt, n, lane);
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
-    if (n + 2 < 8) vop[n + 2] = lds_operand(vt, n + 2, lane);
+    if (n + RA < 8) vop[n + RA] = lds_operand(vt, n + RA, lane);
 #pragma unroll
     for (int qb = 0; qb < QBW; ++qb) O[qb][n] = mfma_f8(vop[n], P[qb], O[qb][n]);
   }
@@ -191,13 +196,13 @@ __device__ __forceinline__ void pv_tile(const uint8_t* vt, const v8i (&P)[QBW], 
 #pragma unroll
     for (int qb = 0; qb < QBW; ++qb) L[qb] = mfma_f8(ones, P[qb], L[qb]);
   }
-  __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
+  if (!PRE) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2 * RA, 0);
 #pragma unroll
-  for (int n = 0; n < 6; ++n) {
+  for (int n = 0; n < 8 - RA; ++n) {
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, QBW, 0);
     __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(SG_MFMA, ROWSUM ? 3 * QBW : 2 * QBW, 0);
+  __builtin_amdgcn_sched_group_barrier(SG_MFMA, ROWSUM ? (RA + 1) * QBW : RA * QBW, 0);
 }
 
 // V-Smooth restore for one tile: its row sum l = 1 * P^T (MFMA; every lane
@@ -351,6 +356,8 @@ __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], co
 // same tile loop half an iteration apart, so that on every SIMD one wave
 // issues MFMAs while the other runs the VALU part:
 //   group A, iteration s:  loads, ExpCast(s) | PV(s), QK(s+1)
+// (group A reads its first PV operands before the ExpCast, so that its MFMA
+// phase starts without an LDS wait)
 //   group B, iteration s:  QK(s), PV(s-1)    | ExpCast(s)
 // Group B starts its MFMAs right after the barrier, at raised priority, so
 // the partner wave's MFMAs do not interleave with them and delay B's ExpCast.
@@ -447,11 +454,18 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   __builtin_amdgcn_s_waitcnt(0);   // this wave's chunks are in LDS
   __syncthreads();
   if (!group_b) qk_tile(kbuf, qop, S, lane);
+  v8i vpre[RA];   // group A: first V operands of its PV, read before its ExpCast
 
   for (int s = 0; s < nT; ++s) {
     const int j = tile_at(s, centre, nT, a.order);
     const int b0 = s & (NBUF - 1), b1 = (s + 1) & (NBUF - 1), bm1 = (s - 1) & (NBUF - 1);
     const bool ld_k = s + 3 < nT, ld_v = s + 2 < nT;
+    if (!group_b) {
+      // V tile s is in LDS since the last barrier: its first operands arrive
+      // while the ExpCast below runs, so the PV MFMAs start without waiting
+#pragma unroll
+      for (int i = 0; i < RA; ++i) vpre[i] = lds_operand(vbuf + b0 * TILE_BYTES, i, lane);
+    }
     // (group A is waves 0-3, threads 0-255)
     if (ld_k && !group_b) load_tile<NTHREADS / 2>(kofs + ((s + 3) & (NBUF - 1)) * TILE_BYTES, kt_ptr(s + 3), voff, wvs);
     if (ld_v && !group_b) load_tile<NTHREADS / 2>(vofs + ((s + 2) & (NBUF - 1)) * TILE_BYTES, vt_ptr(s + 2), voff, wvs);
@@ -461,7 +475,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
     if (!group_b) {
       expcast_tile<DUMP, EXPP>(S, P, aq, skj, M, O, L, j, j == last_masked, a, g, qrow0);
       if (VSMOOTH) vsmooth_tile(mubuf + b0 * MU_SLOT, P, O, L, g);
-      pv_tile<!VSMOOTH>(vbuf + b0 * TILE_BYTES, P, O, L, lane);
+      pv_tile<!VSMOOTH, true>(vbuf + b0 * TILE_BYTES, P, O, L, lane, vpre);
       if (s + 1 < nT) qk_tile(kbuf + b1 * TILE_BYTES, qop, S, lane);
     } else {
       __builtin_amdgcn_s_setprio(2);
