@@ -134,7 +134,10 @@ constexpr int LDS_BYTES = 2 * NBUF * TILE_BYTES;
 // V-Smooth: the tile's scaled block means (128 fp32 = 512 B) ride with each V
 // tile in a 1 KiB slot
 constexpr int MU_SLOT = 1024;
-constexpr int LDS_BYTES_VS = LDS_BYTES + NBUF * MU_SLOT;
+// eight slots: the mean term of four tiles is added at once (vsmooth_flush)
+// while the means of later tiles are being loaded
+constexpr int MU_NBUF = 8;
+constexpr int LDS_BYTES_VS = LDS_BYTES + MU_NBUF * MU_SLOT;
 
 // The 512 bytes of one tile's scaled block means into a 1 KiB LDS slot by one
 // wave's direct load (voff = 16*(lane%32): lanes 32-63 repeat lanes 0-31 into
@@ -205,31 +208,50 @@ __device__ __forceinline__ void pv_tile(const uint8_t* vt, const v8i (&P)[QBW], 
   __builtin_amdgcn_sched_group_barrier(SG_MFMA, ROWSUM ? (RA + 1) * QBW : RA * QBW, 0);
 }
 
-// V-Smooth restore for one tile: its row sum l = 1 * P^T (MFMA; every lane
-// gets the sum of its query), L += l, and O^T[d][q] += (mu_d * inv) * l_q for
-// the tile's block means (the output is multiplied by sv = 1/inv at the end).
-// mu holds the 128 scaled means in lane order: slot 32g + 4n + r is channel
-// 16n + 4g + r, so lane l reads the 32 values of its group g = l/16.
-__device__ __forceinline__ void vsmooth_tile(const uint8_t* mu, const v8i (&P)[QBW], v4f (&O)[QBW][8],
-                                             v4f (&L)[QBW], int g) {
+// V-Smooth restore. The output gains sum_t l_t * mu_t, with l_t the row sum of
+// tile t's weights and mu_t its block means (scaled by inv; the output is
+// multiplied by sv = 1/inv at the end). This is a contraction over tiles, so
+// it runs on the MFMA: four tiles at a time as one v_mfma_f32_16x16x4_f32
+// per 16 channels and 16 queries, O^T[d][q] += sum_k mu_k[d] * l_k[q].
+//
+// vsmooth_tile: the row sum l = 1 * P^T (MFMA; every lane gets the sum of its
+// query), L += l, and l goes to the B operand lb of the batch: lanes of group
+// g = slot hold row k = slot (the tile's place in its batch of four).
+__device__ __forceinline__ void vsmooth_tile(const v8i (&P)[QBW], v4f (&L)[QBW], float (&lb)[QBW], int slot, int g) {
   v8i ones;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = 0x38383838;
-  v4f l[QBW];
 #pragma unroll
   for (int qb = 0; qb < QBW; ++qb) {
-    l[qb] = mfma_f8(ones, P[qb], v4f{0.f, 0.f, 0.f, 0.f});
-    L[qb] += l[qb];
+    const v4f l = mfma_f8(ones, P[qb], v4f{0.f, 0.f, 0.f, 0.f});
+    L[qb] += l;
+    lb[qb] = g == slot ? l[0] : lb[qb];
   }
-  const v4f* m = reinterpret_cast<const v4f*>(mu + 128 * g);
+}
+
+// vsmooth_flush: adds the batch whose last tile is step `last` (slots
+// 0..last%4). Lane (g, i) supplies A[i][g] = mu[16n + i] of the batch's tile g,
+// read from that tile's LDS slot, which holds the 128 scaled means in the
+// order [i][n] (channel 16n + i at 8i + n). Slots past `last` contribute
+// zero; lb is cleared for the next batch.
+__device__ __forceinline__ void vsmooth_flush(const uint8_t* mubuf, int last, v4f (&O)[QBW][8], float (&lb)[QBW],
+                                              int g, int l16) {
+  const int t = last - (last & 3) + g;
+  const bool valid = g <= (last & 3);
+  const v4f* m = reinterpret_cast<const v4f*>(mubuf + (t & (MU_NBUF - 1)) * MU_SLOT + 32 * l16);
+  const v4f m0 = m[0], m1 = m[1];
+  float av[8];
 #pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    const v4f mn = m[n];
-#pragma unroll
-    for (int qb = 0; qb < QBW; ++qb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) O[qb][n][r] = __builtin_fmaf(mn[r], l[qb][0], O[qb][n][r]);
+  for (int r = 0; r < 4; ++r) {
+    av[r] = valid ? m0[r] : 0.0f;
+    av[4 + r] = valid ? m1[r] : 0.0f;
   }
+#pragma unroll
+  for (int n = 0; n < 8; ++n)
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb) O[qb][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[n], lb[qb], O[qb][n], 0, 0, 0);
+#pragma unroll
+  for (int qb = 0; qb < QBW; ++qb) lb[qb] = 0.0f;
 }
 
 // NaN-propagating maximum: scores are finite or -inf, and unlike fmaxf this
@@ -286,8 +308,8 @@ __device__ __forceinline__ uint32_t bytes_exp(const v4f& sc, float a8, float b8)
 // work, with one (rarely taken) rescale branch.
 template <bool DUMP, bool EXPP>
 __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], const float (&aq)[QBW], float skj,
-                                             float (&M)[QBW], v4f (&O)[QBW][8], v4f (&L)[QBW], int j, bool masked,
-                                             const AttnArgs& a, int g, int qrow0) {
+                                             float (&M)[QBW], v4f (&O)[QBW][8], v4f (&L)[QBW], float (&lb)[QBW], int j,
+                                             bool masked, const AttnArgs& a, int g, int qrow0) {
   if (masked) {
     // keys beyond S in the last (ragged) tile take no part in max or sums
 #pragma unroll
@@ -319,6 +341,7 @@ __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], co
         for (int r = 0; r < 4; ++r) O[qb][n][r] = __builtin_ldexpf(O[qb][n][r], d);
 #pragma unroll
       for (int r = 0; r < 4; ++r) L[qb][r] = __builtin_ldexpf(L[qb][r], d);
+      lb[qb] = __builtin_ldexpf(lb[qb], d);   // V-Smooth row sums not yet added
       M[qb] = Mn[qb];
     }
   }
@@ -416,11 +439,12 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
 
   v4f O[QBW][8], L[QBW], S[QBW][8];
   v8i P[QBW];
-  float M[QBW];
+  float M[QBW], lb[QBW];
 #pragma unroll
   for (int qb = 0; qb < QBW; ++qb) {
     L[qb] = v4f{0.f, 0.f, 0.f, 0.f};
     M[qb] = -16384.0f;
+    lb[qb] = 0.0f;
 #pragma unroll
     for (int n = 0; n < 8; ++n) O[qb][n] = v4f{0.f, 0.f, 0.f, 0.f};
   }
@@ -470,20 +494,23 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
     if (ld_k && !group_b) load_tile<NTHREADS / 2>(kofs + ((s + 3) & (NBUF - 1)) * TILE_BYTES, kt_ptr(s + 3), voff, wvs);
     if (ld_v && !group_b) load_tile<NTHREADS / 2>(vofs + ((s + 2) & (NBUF - 1)) * TILE_BYTES, vt_ptr(s + 2), voff, wvs);
     const bool ld_mu = VSMOOTH && ld_v && wv == 0;
-    if (ld_mu) load_means(mofs + ((s + 2) & (NBUF - 1)) * MU_SLOT, mu_ptr(s + 2), voff_mu);
+    if (ld_mu) load_means(mofs + ((s + 2) & (MU_NBUF - 1)) * MU_SLOT, mu_ptr(s + 2), voff_mu);
     const float skj = skp[j];
     if (!group_b) {
-      expcast_tile<DUMP, EXPP>(S, P, aq, skj, M, O, L, j, j == last_masked, a, g, qrow0);
-      if (VSMOOTH) vsmooth_tile(mubuf + b0 * MU_SLOT, P, O, L, g);
+      expcast_tile<DUMP, EXPP>(S, P, aq, skj, M, O, L, lb, j, j == last_masked, a, g, qrow0);
+      if (VSMOOTH) vsmooth_tile(P, L, lb, s & 3, g);
       pv_tile<!VSMOOTH, true>(vbuf + b0 * TILE_BYTES, P, O, L, lane, vpre);
+      if (VSMOOTH && ((s & 3) == 3 || s + 1 == nT)) vsmooth_flush(mubuf, s, O, lb, g, l16);
       if (s + 1 < nT) qk_tile(kbuf + b1 * TILE_BYTES, qop, S, lane);
     } else {
       __builtin_amdgcn_s_setprio(2);
       qk_tile(kbuf + b0 * TILE_BYTES, qop, S, lane);
       if (s > 0) pv_tile<!VSMOOTH>(vbuf + bm1 * TILE_BYTES, P, O, L, lane);
+      // the batch that ended with tile s-1 (before ExpCast(s) may rescale)
+      if (VSMOOTH && s > 0 && ((s - 1) & 3) == 3) vsmooth_flush(mubuf, s - 1, O, lb, g, l16);
       __builtin_amdgcn_s_setprio(0);
-      expcast_tile<DUMP, EXPP>(S, P, aq, skj, M, O, L, j, j == last_masked, a, g, qrow0);
-      if (VSMOOTH) vsmooth_tile(mubuf + b0 * MU_SLOT, P, O, L, g);
+      expcast_tile<DUMP, EXPP>(S, P, aq, skj, M, O, L, lb, j, j == last_masked, a, g, qrow0);
+      if (VSMOOTH) vsmooth_tile(P, L, lb, s & 3, g);
     }
     // group A waits for the loads it issued one iteration ago (a tile is 4
     // loads per thread, plus one for the block means on wave 0 with
@@ -501,7 +528,10 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
     }
     lds_barrier();
   }
-  if (group_b) pv_tile<!VSMOOTH>(vbuf + ((nT - 1) & (NBUF - 1)) * TILE_BYTES, P, O, L, lane);
+  if (group_b) {
+    pv_tile<!VSMOOTH>(vbuf + ((nT - 1) & (NBUF - 1)) * TILE_BYTES, P, O, L, lane);
+    if (VSMOOTH) vsmooth_flush(mubuf, nT - 1, O, lb, g, l16);
+  }
   __builtin_amdgcn_s_waitcnt(0);
 
   float scale = a.sv[2 * bh];

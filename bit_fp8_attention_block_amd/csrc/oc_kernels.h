@@ -26,7 +26,7 @@ struct PrepArgs {
   double* kpart;               // [B][H][nT][128] per-block key sums
   // V-Smooth block means (vmu == nullptr: off)
   uint16_t* vmu;               // [B][H][nT][128] bf16 block means
-  float* vmus;                 // [B][H][nT][128] mean * (448/amax), in attention lane order
+  float* vmus;                 // [B][H][nT][128] mean * (448/amax), channel 16n+i at 8i+n
   // repair (energy == nullptr: no repair)
   double* energy;
   int32_t* sel;

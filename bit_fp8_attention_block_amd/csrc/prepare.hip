@@ -276,7 +276,7 @@ __device__ inline uint4 encode16_sub(uint4 lo, uint4 hi, const float (&mu)[16], 
 // transposed and packed into the PV operand order (through LDS), and with
 // repair the residual energy of every token. With VSMOOTH the codes are of
 // fp32(v - mu) for the tile's block mean mu, and mu * inv is stored in the
-// attention kernel's lane order.
+// order the attention kernel's mean-term MFMA reads it.
 // grid (nT, H, B), 256 threads; thread -> tokens 4m..4m+3 (m = tid/8), channels 16*(tid%8)..+16
 template <bool FP16, bool REPAIR, bool VSMOOTH>
 __global__ __launch_bounds__(256) void prep_v_kernel(PrepArgs a) {
@@ -301,12 +301,10 @@ __global__ __launch_bounds__(256) void prep_v_kernel(PrepArgs a) {
   for (int c = 0; c < 16; ++c)
     mu[c] = VSMOOTH ? bf16_to_f32(a.vmu[((int64_t)bh * a.nT + tile) * HEAD_DIM + 16 * oc + c]) : 0.0f;
   if (VSMOOTH && m == 0) {
-    // mu * inv for channel d = 16n + 4g + r at lane-order slot 32g + 4n + r
+    // mu * inv for channel d = 16n + i at 8i + n (n = oc, i = c here): the
+    // attention kernel's lane i reads its 8 channels as one 32-byte row
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const int d = 16 * oc + c, n = d >> 4, g = (d >> 2) & 3, r = d & 3;
-      a.vmus[((int64_t)bh * a.nT + tile) * HEAD_DIM + 32 * g + 4 * n + r] = mu[c] * inv;
-    }
+    for (int c = 0; c < 16; ++c) a.vmus[((int64_t)bh * a.nT + tile) * HEAD_DIM + 8 * c + oc] = mu[c] * inv;
   }
   uint4 lo[4], hi[4], cd[4];
 #pragma unroll

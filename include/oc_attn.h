@@ -124,9 +124,10 @@ typedef struct oc_attn_desc {
  *   vmu    bf16 [B][H][n_ktiles][128] V block means (V-Smooth only; vpack then
  *                                     holds the codes of v - mean, and sv and
  *                                     vamax refer to those residuals)
- *   vmus   f32 [B][H][n_ktiles][128]  mean * 448/amax in the attention kernel's
- *                                     lane order: slot 32g + 4n + r holds channel
- *                                     16n + 4g + r (V-Smooth only)
+ *   vmus   f32 [B][H][n_ktiles][128]  mean * 448/amax in the order of the
+ *                                     attention kernel's mean-term operand:
+ *                                     slot 8i + n holds channel 16n + i
+ *                                     (V-Smooth only)
  */
 typedef struct oc_attn_ws_layout {
   uint64_t qhat, kpack, vpack, sq, sk, vamax, sv;
