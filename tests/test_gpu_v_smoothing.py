@@ -92,6 +92,35 @@ def test_smoothed_value_attention_matches_oracle(name):
     _compare(q, k, v, out, pairs, rows, label=name + " V-Smooth", prep=prep, v_smooth=True)
 
 
+@pytest.mark.parametrize("S", [1, 5, 130, 300, 700, 1000, 1500])
+def test_smoothed_value_attention_ragged_batches(S):
+    """The mean term is added four key tiles at a time; these lengths give
+    1, 1, 2, 3, 6, 8 and 12 tiles, so the last batch is partial or full in
+    both wave groups, and the last tile is ragged."""
+    oc = _oc()
+    log(f"[v-smooth ragged] S={S}")
+    q, k, v = _biased_values(1, S, 2, seed=11 + S)
+    out = oc.attention(q, k, v, v_smooth=True)
+    prep = oc.prepare(q, k, v, v_smooth=True)
+    torch.cuda.synchronize()
+    _compare(q, k, v, out, [(0, 0), (0, 1)], np.arange(S), label=f"V-Smooth S={S}", prep=prep, v_smooth=True)
+
+
+def test_smoothed_value_attention_full_size_sampled():
+    """S=73397, H=56 (574 key tiles: the last batch holds two), sampled rows of
+    three heads, including the ragged tail."""
+    oc = _oc()
+    name = "s73397_h56"
+    w = workloads.WORKLOADS[name]
+    log(f"[v-smooth full size] {name}")
+    q, k, v = workloads.make_inputs(name, device="cuda")
+    out = oc.attention(q, k, v, v_smooth=True)
+    prep = oc.prepare(q, k, v, v_smooth=True)
+    torch.cuda.synchronize()
+    rows = np.array(workloads.sample_rows(w.S, 64, seed=w.seed))
+    _compare(q, k, v, out, [(0, 0), (0, 29), (0, 55)], rows, label=name + " V-Smooth", prep=prep, v_smooth=True)
+
+
 def test_smoothed_value_attention_with_repair_matches_oracle():
     oc = _oc()
     q, k, v = _biased_values(1, 2000, 2, seed=6)
