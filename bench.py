@@ -79,6 +79,29 @@ def timed_calls(fn, steps, warmup):
     return float(np.mean([a.elapsed_time(b) for a, b in ev])), wall
 
 
+def interleaved_calls(fns, rounds, warmup):
+    """Median ms per call of each function (HIP events on the current
+    stream), the functions called round-robin so that a drift of the board's
+    clock over the run affects all of them alike."""
+    for fn in fns.values():
+        for _ in range(warmup):
+            fn()
+    torch.cuda.synchronize()
+    times = {name: [] for name in fns}
+    for _ in range(rounds):
+        ev = {}
+        for name, fn in fns.items():
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            ev[name] = (a, b)
+        torch.cuda.synchronize()
+        for name, (a, b) in ev.items():
+            times[name].append(a.elapsed_time(b))
+    return {name: float(np.median(t)) for name, t in times.items()}
+
+
 def cpu_baseline(q, k, v, w, rows_n):
     """Oracle on one head: quantize all tokens of that head, then ExpCast
     attention for rows_n sampled query rows against all keys."""
@@ -164,18 +187,17 @@ def main():
                               args.steps, args.warmup)
         print(json.dumps({"kernel_ms": k_ms, "kernel_tflops": flop / k_ms / 1e9, "weights": args.weights}))
         return
-    k_ms, _ = timed_calls(lambda: oc.attention_prepared(prep, with_repair=False, out=out), args.steps, args.warmup)
-    kr_ms, _ = timed_calls(lambda: oc.attention_prepared(prep, with_repair=True, out=out), args.steps, 1)
-    # the same kernel on the byte path ExpCast replaces (exponential + FP8 cast)
-    log("[bench] attention kernel alone, exponential + FP8-cast weights")
-    ke_ms, _ = timed_calls(lambda: oc.attention_prepared(prep, with_repair=False, out=out, weights="exp_fp8"),
-                           args.steps, 1)
-    del prep
-    # the same kernel on a V-Smooth workspace (block means added back per key tile)
-    log("[bench] attention kernel alone, V-Smooth workspace")
+    # with the repair pass, on the byte path ExpCast replaces (exponential +
+    # FP8 cast), and on a V-Smooth workspace; all four taken round-robin
     prep_vs = oc.prepare(q, k, v, v_smooth=True)
-    kvs_ms, _ = timed_calls(lambda: oc.attention_prepared(prep_vs, out=out), args.steps, 1)
-    del prep_vs
+    km = interleaved_calls({
+        "plain": lambda: oc.attention_prepared(prep, with_repair=False, out=out),
+        "repair": lambda: oc.attention_prepared(prep, with_repair=True, out=out),
+        "exp_fp8": lambda: oc.attention_prepared(prep, with_repair=False, out=out, weights="exp_fp8"),
+        "v_smooth": lambda: oc.attention_prepared(prep_vs, out=out),
+    }, args.steps, args.warmup)
+    k_ms, kr_ms, ke_ms, kvs_ms = km["plain"], km["repair"], km["exp_fp8"], km["v_smooth"]
+    del prep, prep_vs
 
     # full call (prepare graph + attention), the headline step
     log("[bench] full call")
@@ -191,10 +213,11 @@ def main():
         step()
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    full_ev_ms, _ = timed_calls(step, args.steps, 0)
-
-    log("[bench] repaired full call")
-    rep_ms, _ = timed_calls(lambda: oc.attention_v_repair(q, k, v, args.repair_budget, out=out), args.steps, 1)
+    log("[bench] full call and repaired full call, round-robin")
+    fm = interleaved_calls({"full": step,
+                            "repair": lambda: oc.attention_v_repair(q, k, v, args.repair_budget, out=out)},
+                           args.steps, 1)
+    full_ev_ms, rep_ms = fm["full"], fm["repair"]
     # prepare alone (the captured graph), HBM-bound
     plan = oc.get_plan(q, None, 0.0)
     ws = oc._workspace(plan, dev)
