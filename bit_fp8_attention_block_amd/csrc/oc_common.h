@@ -20,6 +20,7 @@ constexpr float E4M3_MAX = 448.0f;
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 
 // ---- pack layouts (workspace format, documented in oc_attn.h) ----
 

@@ -345,11 +345,19 @@ __global__ __launch_bounds__(256) void prep_v_kernel(PrepArgs a) {
     for (int r = 0; r < 4; ++r) {
       const uint32_t w[8] = {lo[r].x, lo[r].y, lo[r].z, lo[r].w, hi[r].x, hi[r].y, hi[r].z, hi[r].w};
       const uint32_t cw[4] = {cd[r].x, cd[r].y, cd[r].z, cd[r].w};
+      // decoded codes (the hardware E4M3 -> fp32 conversion is exact)
+      float dec[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const v2f lo2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[j], false);
+        const v2f hi2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[j], true);
+        dec[4 * j] = lo2[0]; dec[4 * j + 1] = lo2[1]; dec[4 * j + 2] = hi2[0]; dec[4 * j + 3] = hi2[1];
+      }
       double e = 0.0;
 #pragma unroll
       for (int c = 0; c < 16; ++c) {
         const float x = __fsub_rn(bits_to_f32<FP16>((w[c >> 1] >> (16 * (c & 1))) & 0xFFFFu), mu[c]);
-        const float t = __fmul_rn(sv, e4m3_decode((cw[c >> 2] >> (8 * (c & 3))) & 0xFFu));
+        const float t = __fmul_rn(sv, dec[c]);
         const double d = (double)__fsub_rn(x, t);
         e = __builtin_fma(d, d, e);
       }
@@ -422,10 +430,31 @@ __global__ __launch_bounds__(1024) void select_kernel(PrepArgs a) {
   for (int shift = 56; shift >= 0; shift -= 8) {
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
-    for (int i = tid; i < S; i += 1024) {
-      const uint64_t u = e[i];
-      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+    // a thread counts runs of equal digits before adding them: the leading
+    // digits of the energies are nearly all alike, and one LDS atomic per
+    // token on a handful of bins would serialise the whole block. Loads go
+    // out eight at a time (one latency per batch, not per token).
+    uint32_t run_bin = 256u, run = 0u;
+    for (int i0 = 0; i0 < S; i0 += 8 * 1024) {
+      uint64_t u[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = i0 + j * 1024 + tid;
+        u[j] = i < S ? e[i] : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (i0 + j * 1024 + tid >= S || (u[j] & mask) != prefix) continue;
+        const uint32_t bin = (uint32_t)(u[j] >> shift) & 255u;
+        if (bin != run_bin) {
+          if (run) atomicAdd(&hist[run_bin], run);
+          run_bin = bin;
+          run = 0u;
+        }
+        ++run;
+      }
     }
+    if (run) atomicAdd(&hist[run_bin], run);
     __syncthreads();
     if (tid == 0) {
       int cum = 0, bin = 255;
@@ -445,10 +474,15 @@ __global__ __launch_bounds__(1024) void select_kernel(PrepArgs a) {
   const int chunk = (S + 1023) / 1024;
   const int i0 = min(S, tid * chunk), i1 = min(S, i0 + chunk);
   int gt = 0, eq = 0;
-  for (int i = i0; i < i1; ++i) {
-    const uint64_t u = e[i];
-    gt += u > prefix;
-    eq += u == prefix;
+  for (int ib = i0; ib < i1; ib += 8) {
+    uint64_t u[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) u[j] = ib + j < i1 ? e[ib + j] : 0u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      gt += ib + j < i1 && u[j] > prefix;
+      eq += ib + j < i1 && u[j] == prefix;
+    }
   }
   int tot;
   const int eq_before = block_exclusive_scan(eq, scratch, tot);
@@ -456,11 +490,18 @@ __global__ __launch_bounds__(1024) void select_kernel(PrepArgs a) {
   int pos = block_exclusive_scan(gt + take_eq, scratch, tot);
   int32_t* sel = a.sel + (int64_t)bh * a.n_sel;
   int taken = 0;
-  for (int i = i0; i < i1; ++i) {
-    const uint64_t u = e[i];
-    if (u > prefix || (u == prefix && taken < take_eq)) {
-      sel[pos++] = i;
-      if (u == prefix) ++taken;
+  if (gt + take_eq > 0) {
+    for (int ib = i0; ib < i1; ib += 8) {
+      uint64_t u[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) u[j] = ib + j < i1 ? e[ib + j] : 0u;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (ib + j < i1 && (u[j] > prefix || (u[j] == prefix && taken < take_eq))) {
+          sel[pos++] = ib + j;
+          if (u[j] == prefix) ++taken;
+        }
+      }
     }
   }
   __threadfence_block();
