@@ -138,10 +138,6 @@ constexpr int MU_SLOT = 1024;
 // while the means of later tiles are being loaded
 constexpr int MU_NBUF = 8;
 constexpr int LDS_BYTES_VS = LDS_BYTES + MU_NBUF * MU_SLOT;
-// repair: the per-key K scales of a residual tile (128 fp32) ride with its
-// residual value tile in a 1 KiB slot, four slots
-constexpr int SC_NBUF = 4;
-constexpr int SC_BYTES = SC_NBUF * MU_SLOT;
 
 // The 512 bytes of one tile's scaled block means into a 1 KiB LDS slot by one
 // wave's direct load (voff = 16*(lane%32): lanes 32-63 repeat lanes 0-31 into
@@ -315,12 +311,17 @@ __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], co
                                              float (&M)[QBW], v4f (&O)[QBW][8], v4f (&L)[QBW], float (&lb)[QBW], int j,
                                              bool masked, const AttnArgs& a, int g, int qrow0) {
   if (masked) {
-    // keys beyond S in the last (ragged) tile take no part in max or sums
+    // keys beyond S in the last (ragged) tile take no part in max or sums.
+    // The empty asm makes lim opaque, so that the 32 compares stay in this
+    // rarely taken branch instead of being hoisted out of the tile loop as
+    // 32 loop-invariant lane masks (64 SGPRs, which then spill).
+    int lim = a.S - j * KTILE - 4 * g;   // this lane's key 16kb + r is dead when 16kb + r >= lim
+    if (!DUMP) asm volatile("" : "+v"(lim));
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const bool dead = j * KTILE + 16 * kb + 4 * g + r >= a.S;
+        const bool dead = 16 * kb + r >= lim;
 #pragma unroll
         for (int qb = 0; qb < QBW; ++qb)
           if (dead) S[qb][kb][r] = -__builtin_inff();
@@ -394,10 +395,14 @@ __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], co
 // in iteration s (K s+3, V s+2) may stay in flight until the end of
 // iteration s+1, which hides L2 misses; so K and V get four LDS buffers each
 // (128 KiB).
+template <bool V>
+struct tail_tag {
+  static constexpr bool value = V;
+};
+
 // End of an iteration: wait for the loads this wave issued one iteration ago
-// (a tile is 4 loads per thread, plus one 1 KiB load on wave 0 for block
-// means or residual K scales), keeping this iteration's in flight; `all`
-// drains everything.
+// (a tile is 4 loads per thread, plus one 1 KiB load on wave 0 for V-Smooth
+// block means), keeping this iteration's in flight; `all` drains everything.
 __device__ __forceinline__ void wait_loads(bool all, bool ld_k, bool ld_v, bool ld_x) {
   if (all) __builtin_amdgcn_s_waitcnt(0x0F70);                               // vmcnt(0)
   else if (ld_k && ld_v) {
@@ -417,7 +422,6 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   uint8_t* const kbuf = smem;
   uint8_t* const vbuf = smem + NBUF * TILE_BYTES;
   uint8_t* const mubuf = smem + 2 * NBUF * TILE_BYTES;   // V-Smooth only
-  uint8_t* const scbuf = mubuf + (VSMOOTH ? MU_NBUF * MU_SLOT : 0);   // repair only
 
   int b, h, qt;
   if (DUMP) {
@@ -440,7 +444,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   const int wvs = __builtin_amdgcn_readfirstlane(wv);
   // LDS offsets of the K, V and block-mean buffers, and the per-lane offsets
   // of the direct loads
-  const uint32_t kofs = lds_offset(kbuf), vofs = lds_offset(vbuf), mofs = lds_offset(mubuf), sofs = lds_offset(scbuf);
+  const uint32_t kofs = lds_offset(kbuf), vofs = lds_offset(vbuf), mofs = lds_offset(mubuf);
   const uint32_t voff = 16u * tid, voff_mu = 16u * (lane & 31);
   const int q0 = qt * BQ + wv * QBW * 16;
   const int qrow0 = q0 + l16;
@@ -480,34 +484,15 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   const int centre = (nT - 1) >> 1;
   const int last_masked = (a.S & (KTILE - 1)) ? nT - 1 : -1;
 
-  // Steps 0..nT-1 visit the key tiles; with the repair, steps nT..nS-1 are
-  // the residual tiles (selected K rows and residual value codes), which
-  // stream through the same buffers and load schedule.
-  const int nR = REPAIR ? a.n_sel_tiles : 0, nS = nT + nR;
-  const uint8_t* ksb = a.kselpack + (int64_t)bh * nR * TILE_BYTES;
-  const uint8_t* rsb = a.rpack + (int64_t)bh * nR * TILE_BYTES;
-  const float* sks = a.sksel + (int64_t)bh * nR * KTILE;
-  const auto kt_ptr = [&](int step) {
-    return step < nT ? kg + (int64_t)tile_at(step, centre, nT, a.order) * TILE_BYTES
-                     : ksb + (int64_t)(step - nT) * TILE_BYTES;
-  };
-  const auto vt_ptr = [&](int step) {
-    return step < nT ? vg + (int64_t)tile_at(step, centre, nT, a.order) * TILE_BYTES
-                     : rsb + (int64_t)(step - nT) * TILE_BYTES;
-  };
-  const auto sc_ptr = [&](int step) { return reinterpret_cast<const uint8_t*>(sks + (step - nT) * KTILE); };
+  const auto kt_ptr = [&](int step) { return kg + (int64_t)tile_at(step, centre, nT, a.order) * TILE_BYTES; };
+  const auto vt_ptr = [&](int step) { return vg + (int64_t)tile_at(step, centre, nT, a.order) * TILE_BYTES; };
   // prologue: K steps 0..2 and V steps 0..1
 #pragma unroll
   for (int i = 0; i < 3; ++i)
-    if (i < nS) load_tile<NTHREADS>(kofs + i * TILE_BYTES, kt_ptr(i), voff, wvs);
+    if (i < nT) load_tile<NTHREADS>(kofs + i * TILE_BYTES, kt_ptr(i), voff, wvs);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
-    if (i < nS) load_tile<NTHREADS>(vofs + i * TILE_BYTES, vt_ptr(i), voff, wvs);
-  if (REPAIR && wv == 0) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      if (i >= nT && i < nS) load_means(sofs + i * MU_SLOT, sc_ptr(i), voff_mu);
-  }
+    if (i < nT) load_tile<NTHREADS>(vofs + i * TILE_BYTES, vt_ptr(i), voff, wvs);
   const auto mu_ptr = [&](int step) {
     return reinterpret_cast<const uint8_t*>(a.vmus + ((int64_t)bh * nT + tile_at(step, centre, nT, a.order)) * HEAD_DIM);
   };
@@ -521,10 +506,13 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   if (!group_b) qk_tile(kbuf, qop, S, lane);
   v8i vpre[RA];   // group A: first V operands of its PV, read before its ExpCast
 
-  for (int s = 0; s < nT; ++s) {
+  // One iteration of the tile loop. Before the last three steps (TAIL
+  // false) every tile load is issued, so the load flags are constants.
+  const auto iteration = [&](int s, auto tail) {
+    constexpr bool TAIL = decltype(tail)::value;
     const int j = tile_at(s, centre, nT, a.order);
     const int b0 = s & (NBUF - 1), b1 = (s + 1) & (NBUF - 1), bm1 = (s - 1) & (NBUF - 1);
-    const bool ld_k = s + 3 < nS, ld_v = s + 2 < nS;
+    const bool ld_k = !TAIL || s + 3 < nT, ld_v = !TAIL || s + 2 < nT;
     if (!group_b) {
       // V tile s is in LDS since the last barrier: its first operands arrive
       // while the ExpCast below runs, so the PV MFMAs start without waiting
@@ -534,13 +522,9 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
     // (group A is waves 0-3, threads 0-255)
     if (ld_k && !group_b) load_tile<NTHREADS / 2>(kofs + ((s + 3) & (NBUF - 1)) * TILE_BYTES, kt_ptr(s + 3), voff, wvs);
     if (ld_v && !group_b) load_tile<NTHREADS / 2>(vofs + ((s + 2) & (NBUF - 1)) * TILE_BYTES, vt_ptr(s + 2), voff, wvs);
-    // one more 1 KiB load on wave 0: the block means of key tile s+2, or the
-    // K scales of residual step s+2
-    const bool ld_mu = VSMOOTH && s + 2 < nT && wv == 0;
-    const bool ld_sc = REPAIR && s + 2 >= nT && ld_v && wv == 0;
+    // V-Smooth: one more 1 KiB load on wave 0, the block means of tile s+2
+    const bool ld_mu = VSMOOTH && ld_v && wv == 0;
     if (ld_mu) load_means(mofs + ((s + 2) & (MU_NBUF - 1)) * MU_SLOT, mu_ptr(s + 2), voff_mu);
-    if (ld_sc) load_means(sofs + ((s + 2) & (SC_NBUF - 1)) * MU_SLOT, sc_ptr(s + 2), voff_mu);
-    const bool ld_x = ld_mu || ld_sc;
     const float skj = skp[j];
     if (!group_b) {
       expcast_tile<DUMP, EXPP>(S, P, aq, skj, M, O, L, lb, j, j == last_masked, a, g, qrow0);
@@ -562,9 +546,12 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
     // loads per thread, plus one for the block means on wave 0 with
     // V-Smooth); this iteration's stay in flight. The code dump's stores also
     // count, so that path drains everything.
-    wait_loads(DUMP || group_b, ld_k, ld_v, ld_x);
+    wait_loads(DUMP || group_b, ld_k, ld_v, ld_mu);
     lds_barrier();
-  }
+  };
+  int s = 0;
+  for (; s < nT - 3; ++s) iteration(s, tail_tag<false>{});
+  for (; s < nT; ++s) iteration(s, tail_tag<true>{});
   if (group_b) {
     pv_tile<!VSMOOTH>(vbuf + ((nT - 1) & (NBUF - 1)) * TILE_BYTES, P, O, L, lane);
     if (VSMOOTH) vsmooth_flush(mubuf, nT - 1, O, lb, g, l16);
@@ -582,47 +569,55 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int n = 0; n < 8; ++n) O[qb][n] *= rs;
     scale = sr;
-    for (int s = nT; s < nS; ++s) {
-      const int b0 = s & (NBUF - 1);
-      const bool ld_k = s + 3 < nS, ld_v = s + 2 < nS, ld_sc = ld_v && wv == 0;
-      if (ld_k && !group_b) load_tile<NTHREADS / 2>(kofs + ((s + 3) & (NBUF - 1)) * TILE_BYTES, kt_ptr(s + 3), voff, wvs);
-      if (ld_v && !group_b) load_tile<NTHREADS / 2>(vofs + ((s + 2) & (NBUF - 1)) * TILE_BYTES, vt_ptr(s + 2), voff, wvs);
-      if (ld_sc) load_means(sofs + ((s + 2) & (SC_NBUF - 1)) * MU_SLOT, sc_ptr(s + 2), voff_mu);
-      // this lane's per-key K scales: keys 16kb + 4g + r (slots past n_sel
-      // are padding and get no weight)
-      const v4f* skv = reinterpret_cast<const v4f*>(scbuf + (s & (SC_NBUF - 1)) * MU_SLOT) + g;
-      qk_tile(kbuf + b0 * TILE_BYTES, qop, S, lane);
+    const int nslot = a.n_sel_tiles * KTILE;
+    const uint8_t* ksb = a.kselpack + (int64_t)bh * a.n_sel_tiles * TILE_BYTES;
+    const uint8_t* rsb = a.rpack + (int64_t)bh * a.n_sel_tiles * TILE_BYTES;
+    const float* sks = a.sksel + (int64_t)bh * nslot;
+    for (int ts = 0; ts < a.n_sel_tiles; ++ts) {
+      __syncthreads();   // every wave is done with the buffers about to be overwritten
+      load_tile<NTHREADS>(kofs, ksb + (int64_t)ts * TILE_BYTES, voff, wvs);
+      load_tile<NTHREADS>(vofs, rsb + (int64_t)ts * TILE_BYTES, voff, wvs);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) {
-        const v4f sk4 = skv[4 * kb];
+        const v8i kop = lds_operand(kbuf, kb, lane);
+        float skk[4];
         bool live[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) live[r] = (s - nT) * KTILE + 16 * kb + 4 * g + r < a.n_sel;
+        for (int r = 0; r < 4; ++r) {
+          const int slot = ts * KTILE + 16 * kb + 4 * g + r;
+          skk[r] = sks[slot];
+          live[r] = slot < a.n_sel;
+        }
 #pragma unroll
         for (int qb = 0; qb < QBW; ++qb) {
-          const v4f sc = S[qb][kb];
+          const v4f sc = mfma_f8(kop, qop[qb], v4f{0.f, 0.f, 0.f, 0.f});
           uint32_t w = 0;
           if (EXPP) {
             float e[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              e[r] = live[r] ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], aq[qb] * sk4[r] * 0.125f, 8.0f - M[qb]))
+              e[r] = live[r] ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], aq[qb] * skk[r] * 0.125f, 8.0f - M[qb]))
                              : 0.0f;
             w = bytes_exp_fp8(e[0], e[1], e[2], e[3]);
           } else {
             const float bq = __builtin_fmaf(-8.0f, M[qb], EXPCAST_C);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const float y = live[r] ? __builtin_fmaf(sc[r], aq[qb] * sk4[r], bq) : -1.0f;
+              const float y = live[r] ? __builtin_fmaf(sc[r], aq[qb] * skk[r], bq) : -1.0f;
               w = __builtin_amdgcn_cvt_pk_u8_f32(y, r, w);
             }
           }
           P[qb][kb] = (int)w;
         }
       }
-      pv_tile<false>(vbuf + b0 * TILE_BYTES, P, O, L, lane);
-      wait_loads(group_b, ld_k, ld_v, ld_sc);
-      lds_barrier();
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const v8i rop = lds_operand(vbuf, n, lane);
+#pragma unroll
+        for (int qb = 0; qb < QBW; ++qb) O[qb][n] = mfma_f8(rop, P[qb], O[qb][n]);
+      }
     }
   }
 
@@ -644,7 +639,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
 
 template <bool REPAIR, bool DUMP, bool EXPP, bool VSMOOTH>
 static hipError_t launch_one(const AttnArgs& a, dim3 grid, hipStream_t st) {
-  constexpr int lds = (VSMOOTH ? LDS_BYTES_VS : LDS_BYTES) + (REPAIR ? SC_BYTES : 0);
+  constexpr int lds = VSMOOTH ? LDS_BYTES_VS : LDS_BYTES;
   static bool configured = false;
   if (!configured) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<REPAIR, DUMP, EXPP, VSMOOTH>),
