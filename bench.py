@@ -40,7 +40,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 # rocprofv3 PMC counters (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors a
 # plain 4 GiB copy gives; profiles/attn_kernel_s73397_h56.md). They are only
 # reported while the kernel sources still hash to the measured version.
-MEASURED_TRAFFIC = {"sources_sha256": "b2e1f8f26202df0609e516ef519bbcd95cdb4145c43bc7c94772b7747c0a592b", "bytes": 11964975456}
+MEASURED_TRAFFIC = {"sources_sha256": "3942e4250c22c7a718d988580086ae4d288467c6fb2597309fa22770cbd907ab", "bytes": 11978758261}
 KERNEL_SOURCES = ("bit_fp8_attention_block_amd/csrc/attention.hip", "bit_fp8_attention_block_amd/csrc/oc_common.h")
 
 
