@@ -171,3 +171,19 @@ def test_prepared_call_follows_the_workspace_setting():
     plain = oc.attention(q, k, v)
     torch.cuda.synchronize()
     assert torch.equal(a, full) and torch.equal(b, plain) and not torch.equal(a, b)
+
+
+@pytest.mark.parametrize("S,fp16", [(300, False), (1000, True)])
+def test_all_options_together_match_oracle(S, fp16):
+    """The comparison byte path with K-mean smoothing, V-Smooth and repair in
+    one call (three and eight key tiles, bf16 and fp16 inputs)."""
+    oc = _oc()
+    log(f"[all options] S={S} fp16={fp16}")
+    q, k, v = _biased_values(1, S, 2, seed=40 + S, dtype=torch.float16 if fp16 else torch.bfloat16)
+    k = k + 2.0   # a shared key offset for the smoothing to remove
+    opts = dict(weights="exp_fp8", k_smooth=True, v_smooth=True)
+    out = oc.attention_v_repair(q, k, v, 0.02, **opts)
+    prep = oc.prepare_v_repair(q, k, v, 0.02, k_smooth=True, v_smooth=True)
+    torch.cuda.synchronize()
+    _compare(q, k, v, out, [(0, 0), (0, 1)], np.arange(S), budget=0.02, label=f"all options S={S}", prep=prep,
+             weights="exp_cast", k_smooth=True, v_smooth=True)
