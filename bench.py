@@ -164,8 +164,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the path has no multi-GPU mode (heads would shard with no "
-              "communication; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the path has no multi-GPU mode (the (batch, head) pairs would "
+              "shard across GPUs with no communication). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import bit_fp8_attention_block_amd as oc

@@ -21,7 +21,7 @@ Sources (the pages this follows):
     quantized residual of the worst-rounded value tokens, chosen by residual
     energy, with a token budget (0.005 in the example).
 
-Readings where the pages leave a step open (each is listed in the design doc):
+Readings where the pages leave a step open:
   * weights are stored as 256*p, p = 2^(x - M) relative to the row max, so the
     code is 8*(x - M) + 120 + beta; the largest weight lands on code 120.
   * the byte is the round-to-nearest-even of that affine value, clamped to the
