@@ -379,22 +379,7 @@ __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], co
   }
 }
 
-// One workgroup = 256 queries of one (b, h): 8 waves of 32 queries. Waves
-// 0-3 (group A) and 4-7 (group B) share the SIMDs pairwise and run the
-// same tile loop half an iteration apart, so that on every SIMD one wave
-// issues MFMAs while the other runs the VALU part:
-//   group A, iteration s:  loads, ExpCast(s) | PV(s), QK(s+1)
-// (group A reads its first PV operands before the ExpCast, so that its MFMA
-// phase starts without an LDS wait)
-//   group B, iteration s:  QK(s), PV(s-1)    | ExpCast(s)
-// Group B starts its MFMAs right after the barrier, at raised priority, so
-// the partner wave's MFMAs do not interleave with them and delay B's ExpCast.
-// Only group A issues the tile loads (issuing the 32 KiB of one iteration
-// takes several hundred cycles, which would otherwise hold back B's MFMAs).
-// Iteration s reads K tiles s and s+1 and V tiles s-1 and s. The loads issued
-// in iteration s (K s+3, V s+2) may stay in flight until the end of
-// iteration s+1, which hides L2 misses; so K and V get four LDS buffers each
-// (128 KiB).
+// the two parts of the tile loop (see the kernel)
 template <bool V>
 struct tail_tag {
   static constexpr bool value = V;
@@ -416,6 +401,22 @@ __device__ __forceinline__ void wait_loads(bool all, bool ld_k, bool ld_v, bool 
   }
 }
 
+// One workgroup = 256 queries of one (b, h): 8 waves of 32 queries. Waves
+// 0-3 (group A) and 4-7 (group B) share the SIMDs pairwise and run the
+// same tile loop half an iteration apart, so that on every SIMD one wave
+// issues MFMAs while the other runs the VALU part:
+//   group A, iteration s:  loads, ExpCast(s) | PV(s), QK(s+1)
+// (group A reads its first PV operands before the ExpCast, so that its MFMA
+// phase starts without an LDS wait)
+//   group B, iteration s:  QK(s), PV(s-1)    | ExpCast(s)
+// Group B starts its MFMAs right after the barrier, at raised priority, so
+// the partner wave's MFMAs do not interleave with them and delay B's ExpCast.
+// Only group A issues the tile loads (issuing the 32 KiB of one iteration
+// takes several hundred cycles, which would otherwise hold back B's MFMAs).
+// Iteration s reads K tiles s and s+1 and V tiles s-1 and s. The loads issued
+// in iteration s (K s+3, V s+2) may stay in flight until the end of
+// iteration s+1, which hides L2 misses; so K and V get four LDS buffers each
+// (128 KiB).
 template <bool REPAIR, bool DUMP, bool EXPP, bool VSMOOTH>
 __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
