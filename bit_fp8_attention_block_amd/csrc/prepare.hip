@@ -510,8 +510,8 @@ __global__ __launch_bounds__(1024) void select_kernel(PrepArgs a) {
   // residual amax over the selected tokens (8-channel chunks)
   const float sv = a.sv[2 * bh], inv = a.sv[2 * bh + 1];
   float mx = 0.0f;
-  for (int it = tid; it < k * 16; it += 1024) {
-    const int slot = it >> 4, c8 = (it & 15) * 8;
+  for (int64_t it = tid; it < (int64_t)k * 16; it += 1024) {
+    const int slot = (int)(it >> 4), c8 = (int)(it & 15) * 8;
     const int tok = sel[slot];
     const int64_t off = (int64_t)b * a.sb + (int64_t)tok * a.ss + (int64_t)h * a.sh + c8;
     const uint4 w = *reinterpret_cast<const uint4*>(a.v + off);

@@ -56,6 +56,15 @@ def test_plan_create_rejects(kw, status):
     assert st == status and not p.value
 
 
+def test_plan_create_rejects_grids_past_the_launch_limit():
+    """B*H*ceil(S/256) attention workgroups must fit the 32-bit grid index."""
+    st, p = create(make_desc(B=1, S=2**30, H=64))
+    assert st == oc.OC_ERR_UNSUPPORTED and not p.value
+    st, p = create(make_desc(B=1, S=2**30 - 256 * 16, H=16))
+    assert st == oc.OC_OK and p.value
+    lib.oc_attn_plan_destroy(p)
+
+
 @pytest.mark.parametrize("budget", [-0.1, 1.01, math.nan])
 def test_plan_create_rejects_budget(budget):
     st, p = create(make_desc(), budget)
