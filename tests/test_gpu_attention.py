@@ -65,7 +65,7 @@ def check_max_trace(kernel_trace, own, x, bound, order="mid"):
 
 
 def _compare(q, k, v, out, pairs, rows, budget=0.0, tol=TOL, label="", order="mid", prep=None, weights="expcast",
-             k_smooth=False, v_smooth=False):
+             k_smooth=False, v_smooth=False, tau=None):
     """rel-L2 of the kernel's rows against the single-pass oracle. With a
     prepared workspace, the oracle replays the running-max decisions the
     kernel made (read back through the debug dump), after checking that each
@@ -78,17 +78,17 @@ def _compare(q, k, v, out, pairs, rows, budget=0.0, tol=TOL, label="", order="mi
             oc = _oc()
             _, m_used, _ = oc.debug_pcodes(prep, b, h, with_codes=False, weights=KERNEL_WEIGHTS[weights])
             m_trace = m_used[torch.as_tensor(rows, device=m_used.device)].cpu().numpy()
-            own = oracle_rows(q, k, v, b, h, rows, budget=budget, order=order, weights=weights, k_smooth=k_smooth,
-                              v_smooth=v_smooth)
-            tau = 1 / math.sqrt(128)
-            x = oracle.log2_logits(own["ph"], rows, tau)
-            nflip += check_max_trace(m_trace, own["m_trace"], x, logit_error_bound(own["ph"], rows, tau), order)
-        r = oracle_rows(q, k, v, b, h, rows, budget=budget, order=order, m_trace=m_trace, weights=weights,
+            own = oracle_rows(q, k, v, b, h, rows, budget=budget, tau=tau, order=order, weights=weights,
+                              k_smooth=k_smooth, v_smooth=v_smooth)
+            t = tau if tau else 1 / math.sqrt(128)
+            x = oracle.log2_logits(own["ph"], rows, t)
+            nflip += check_max_trace(m_trace, own["m_trace"], x, logit_error_bound(own["ph"], rows, t), order)
+        r = oracle_rows(q, k, v, b, h, rows, budget=budget, tau=tau, order=order, m_trace=m_trace, weights=weights,
                         k_smooth=k_smooth, v_smooth=v_smooth)
         got = out_rows(out, b, h, rows)
         e = oracle.rel_l2(got, r["out"])
         errs.append(e)
-        r2 = oracle.expcast_attention_head(head64(q, b, h), head64(k, b, h), head64(v, b, h), rows=rows,
+        r2 = oracle.expcast_attention_head(head64(q, b, h), head64(k, b, h), head64(v, b, h), tau=tau, rows=rows,
                                            ph=r["ph"], weights=weights)
         two.append(oracle.rel_l2(got, r2["out"]))
         assert np.isfinite(got).all()
