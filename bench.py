@@ -143,7 +143,7 @@ def main():
     ap.add_argument("--workload", default=workloads.HEADLINE, choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--budget", type=float, default=0.0, help="V-repair budget of the timed full call")
     ap.add_argument("--repair-budget", type=float, default=0.005, help="budget of the extra repaired measurement")
-    ap.add_argument("--cpu-rows", type=int, default=8192)
+    ap.add_argument("--cpu-rows", type=int, default=10240)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparator", action="store_true")
     ap.add_argument("--kernel-only", action="store_true", help="time only the attention kernel (for profiling)")
