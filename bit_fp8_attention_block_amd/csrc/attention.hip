@@ -116,16 +116,6 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-__device__ inline float max_over_row_lanes(float m) {
-  // the 4 lanes l, l^16, l^32, l^48 hold the same query
-  const uint32_t u = __float_as_uint(m);
-  auto s16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  m = __builtin_elementwise_maximum(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
-  const uint32_t u2 = __float_as_uint(m);
-  auto s32 = __builtin_amdgcn_permlane32_swap(u2, u2, false, false);
-  return __builtin_elementwise_maximum(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
-}
-
 constexpr int QBW = 2;            // 16-query blocks per wave
 constexpr int NWAVES = 8;         // 2 waves per SIMD: one of each group
 constexpr int NTHREADS = 64 * NWAVES;
@@ -301,15 +291,43 @@ __device__ __forceinline__ uint32_t bytes_exp(const v4f& sc, float a8, float b8)
                        __builtin_amdgcn_exp2f(__builtin_fmaf(sc[3], a8, b8)));
 }
 
+// The 4 lanes of a query are l, l^16, l^32, l^48: the same position in the
+// four 16-lane rows of the wave. Exchanges of whole rows between two
+// registers (v_permlane16_swap: rows 1, 3 of the first with rows 0, 2 of the
+// second; v_permlane32_swap: rows 2, 3 of the first with rows 0, 1 of the
+// second) let both 16-query blocks share each step.
+__device__ __forceinline__ uint32_t f2u(float x) { return __float_as_uint(x); }
+__device__ __forceinline__ float u2f(uint32_t x) { return __uint_as_float(x); }
+
+// Max over the 4 lanes of each query of x0 (block 0) and x1 (block 1): the
+// result holds block 0's maxima in rows 0 and 2 and block 1's in rows 1 and 3.
+__device__ __forceinline__ float row_max_pair(float x0, float x1) {
+  const auto s16 = __builtin_amdgcn_permlane16_swap(f2u(x0), f2u(x1), false, false);
+  const float c = fmax_p(u2f(s16[0]), u2f(s16[1]));   // rows: b0 of rows 0-1, b1 of rows 0-1, b0 of 2-3, b1 of 2-3
+  const auto s32 = __builtin_amdgcn_permlane32_swap(f2u(c), f2u(c), false, false);
+  return fmax_p(u2f(s32[0]), u2f(s32[1]));
+}
+
+// A value held per block as above (block = row parity) -> both blocks' values
+// in every lane.
+__device__ __forceinline__ void spread_pair(float v, float& v0, float& v1) {
+  const auto s16 = __builtin_amdgcn_permlane16_swap(f2u(v), f2u(v), false, false);
+  v0 = u2f(s16[0]);
+  v1 = u2f(s16[1]);
+}
+
 // ExpCast for one tile and the wave's two 16-query blocks: raise the running
 // bit-aligned max (rescaling O and L by the exact power of two when it
 // grows), then one FMA and one saturating convert per score give the E4M3
-// bytes. Both blocks are handled side by side to give the VALU independent
-// work, with one (rarely taken) rescale branch.
+// bytes. The running max Mv is kept per block by row parity (rows 0, 2:
+// block 0; rows 1, 3: block 1), so that the max, the ceiling, the growth
+// test and the FMA addend take one instruction for both blocks. aq8 is
+// 8*tau*log2(e)*sq/8 for the wave's 32 queries, which share one 128-query
+// scale block.
 template <bool DUMP, bool EXPP>
-__device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], const float (&aq)[QBW], float skj,
-                                             float (&M)[QBW], v4f (&O)[QBW][8], v4f (&L)[QBW], float (&lb)[QBW], int j,
-                                             bool masked, const AttnArgs& a, int g, int qrow0) {
+__device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], float aq8, float skj, float& Mv,
+                                             v4f (&O)[QBW][8], v4f (&L)[QBW], float (&lb)[QBW], int j, bool masked,
+                                             const AttnArgs& a, int g, int qrow0) {
   if (masked) {
     // keys beyond S in the last (ragged) tile take no part in max or sums.
     // The empty asm makes lim opaque, so that the 32 compares stay in this
@@ -327,39 +345,41 @@ __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], co
           if (dead) S[qb][kb][r] = -__builtin_inff();
       }
   }
-  float aqs[QBW], Mn[QBW];
-  bool grow = false;
-#pragma unroll
-  for (int qb = 0; qb < QBW; ++qb) {
-    aqs[qb] = aq[qb] * skj;
-    const float m = max_over_row_lanes(lane_max32(S[qb]));
-    Mn[qb] = fmax_p(M[qb], __builtin_ceilf((aqs[qb] * m) * 0.125f));
-    grow |= Mn[qb] > M[qb];
-  }
-  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+  static_assert(QBW == 2, "the per-block exchanges assume two 16-query blocks per wave");
+  const float aqs8 = aq8 * skj;   // a/8, a = 8*tau*log2(e)*sq*sk
+  const float mv = row_max_pair(lane_max32(S[0]), lane_max32(S[1]));
+  const float Mn = fmax_p(Mv, __builtin_ceilf(aqs8 * mv));
+  if (__builtin_amdgcn_ballot_w64(Mn > Mv) != 0) {
+    float d0, d1;   // exponent change of each block (<= 0)
+    spread_pair(Mv - Mn, d0, d1);
+    const int d[QBW] = {(int)d0, (int)d1};
 #pragma unroll
     for (int qb = 0; qb < QBW; ++qb) {
-      const int d = (int)(M[qb] - Mn[qb]);   // <= 0
 #pragma unroll
       for (int n = 0; n < 8; ++n)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) O[qb][n][r] = __builtin_ldexpf(O[qb][n][r], d);
+        for (int r = 0; r < 4; ++r) O[qb][n][r] = __builtin_ldexpf(O[qb][n][r], d[qb]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) L[qb][r] = __builtin_ldexpf(L[qb][r], d);
-      lb[qb] = __builtin_ldexpf(lb[qb], d);   // V-Smooth row sums not yet added
-      M[qb] = Mn[qb];
+      for (int r = 0; r < 4; ++r) L[qb][r] = __builtin_ldexpf(L[qb][r], d[qb]);
+      lb[qb] = __builtin_ldexpf(lb[qb], d[qb]);   // V-Smooth row sums not yet added
     }
+    Mv = Mn;
   }
+  float b[QBW];   // the FMA's addend per block, in every lane
+  spread_pair(EXPP ? 8.0f - Mn : __builtin_fmaf(-8.0f, Mn, EXPCAST_C), b[0], b[1]);
+  const float aqs = aqs8 * 8.0f;
 #pragma unroll
   for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
     for (int qb = 0; qb < QBW; ++qb) {
       if (EXPP)
-        P[qb][kb] = (int)bytes_exp(S[qb][kb], aqs[qb] * 0.125f, 8.0f - Mn[qb]);
+        P[qb][kb] = (int)bytes_exp(S[qb][kb], aqs8, b[qb]);
       else
-        P[qb][kb] = (int)bytes_expcast(S[qb][kb], aqs[qb], __builtin_fmaf(-8.0f, Mn[qb], EXPCAST_C));
+        P[qb][kb] = (int)bytes_expcast(S[qb][kb], aqs, b[qb]);
     }
   if (DUMP) {
+    float mq[QBW];
+    spread_pair(Mn, mq[0], mq[1]);
 #pragma unroll
     for (int qb = 0; qb < QBW; ++qb) {
       const int qrow = qrow0 + 16 * qb;
@@ -373,7 +393,7 @@ __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], co
               if (key < a.S) a.dump_codes[(int64_t)qrow * a.S + key] = (uint8_t)((uint32_t)P[qb][kb] >> (8 * r));
             }
         }
-        if (g == 0) a.dump_m[(int64_t)qrow * a.nT + j] = (int32_t)Mn[qb];
+        if (g == 0) a.dump_m[(int64_t)qrow * a.nT + j] = (int32_t)mq[qb];
       }
     }
   }
@@ -453,7 +473,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
 
   // Q^T operands stay in registers for the whole loop
   v8i qop[QBW];
-  float aq[QBW];
+  float aq[QBW];   // equal: the wave's 32 queries lie in one 128-query scale block
 #pragma unroll
   for (int qb = 0; qb < QBW; ++qb) {
     const uint8_t* p = a.qhat + ((int64_t)bh * a.s_pad_q + q0 + 16 * qb + l16) * HEAD_DIM + 32 * g;
@@ -466,11 +486,11 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
 
   v4f O[QBW][8], L[QBW], S[QBW][8];
   v8i P[QBW];
-  float M[QBW], lb[QBW];
+  float Mv = -16384.0f, lb[QBW];   // running max per block by row parity (see expcast_tile)
+  const float aq8 = aq[0] * 0.125f;
 #pragma unroll
   for (int qb = 0; qb < QBW; ++qb) {
     L[qb] = v4f{0.f, 0.f, 0.f, 0.f};
-    M[qb] = -16384.0f;
     lb[qb] = 0.0f;
 #pragma unroll
     for (int n = 0; n < 8; ++n) O[qb][n] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -528,7 +548,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
     if (ld_mu) load_means(mofs + ((s + 2) & (MU_NBUF - 1)) * MU_SLOT, mu_ptr(s + 2), voff_mu);
     const float skj = skp[j];
     if (!group_b) {
-      expcast_tile<DUMP, EXPP>(S, P, aq, skj, M, O, L, lb, j, j == last_masked, a, g, qrow0);
+      expcast_tile<DUMP, EXPP>(S, P, aq8, skj, Mv, O, L, lb, j, j == last_masked, a, g, qrow0);
       if (VSMOOTH) vsmooth_tile(P, L, lb, s & 3, g);
       pv_tile<!VSMOOTH, true>(vbuf + b0 * TILE_BYTES, P, O, L, lane, vpre);
       if (VSMOOTH && ((s & 3) == 3 || s + 1 == nT)) vsmooth_flush(mubuf, s, O, lb, g, l16);
@@ -540,7 +560,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
       // the batch that ended with tile s-1 (before ExpCast(s) may rescale)
       if (VSMOOTH && s > 0 && ((s - 1) & 3) == 3) vsmooth_flush(mubuf, s - 1, O, lb, g, l16);
       __builtin_amdgcn_s_setprio(0);
-      expcast_tile<DUMP, EXPP>(S, P, aq, skj, M, O, L, lb, j, j == last_masked, a, g, qrow0);
+      expcast_tile<DUMP, EXPP>(S, P, aq8, skj, Mv, O, L, lb, j, j == last_masked, a, g, qrow0);
       if (VSMOOTH) vsmooth_tile(P, L, lb, s & 3, g);
     }
     // group A waits for the loads it issued one iteration ago (a tile is 4
@@ -565,6 +585,8 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
     // and without touching L: O = sv*sum P v_hat + sr*sum P r_hat
     const float sr = a.sr[2 * bh];
     const float rs = scale / sr;
+    float M[QBW];   // final running max of each block, in every lane
+    spread_pair(Mv, M[0], M[1]);
 #pragma unroll
     for (int qb = 0; qb < QBW; ++qb)
 #pragma unroll
