@@ -172,10 +172,7 @@ __device__ __forceinline__ void qk_tile(const uint8_t* kt, const v8i (&qop)[QBW]
 // read-ahead. With PRE the first RA operands were read by the caller (pre).
 template <bool ROWSUM = true, bool PRE = false>
 __device__ __forceinline__ void pv_tile(const uint8_t* vt, const v8i (&P)[QBW], v4f (&O)[QBW][8], v4f (&L)[QBW],
-                                        int lane, const v8i* pre = nullptr) {
-  v8i ones;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = 0x38383838;   // E4M3 1.0
+                                        int lane, const v8i& ones, const v8i* pre = nullptr) {
   v8i vop[8];
 #pragma unroll
   for (int n = 0; n < RA; ++n) vop[n] = PRE ? pre[n] : lds_operand(vt, n, lane);
@@ -207,10 +204,8 @@ __device__ __forceinline__ void pv_tile(const uint8_t* vt, const v8i (&P)[QBW], 
 // vsmooth_tile: the row sum l = 1 * P^T (MFMA; every lane gets the sum of its
 // query), L += l, and l goes to the B operand lb of the batch: lanes of group
 // g = slot hold row k = slot (the tile's place in its batch of four).
-__device__ __forceinline__ void vsmooth_tile(const v8i (&P)[QBW], v4f (&L)[QBW], float (&lb)[QBW], int slot, int g) {
-  v8i ones;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = 0x38383838;
+__device__ __forceinline__ void vsmooth_tile(const v8i (&P)[QBW], v4f (&L)[QBW], float (&lb)[QBW], int slot, int g,
+                                             const v8i& ones) {
 #pragma unroll
   for (int qb = 0; qb < QBW; ++qb) {
     const v4f l = mfma_f8(ones, P[qb], v4f{0.f, 0.f, 0.f, 0.f});
@@ -484,6 +479,12 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
     aq[qb] = a.c8 * a.sq[(int64_t)bh * a.nQB + ((q0 + 16 * qb) >> 7)];
   }
 
+  // the all-ones operand of the row-sum MFMAs (E4M3 1.0 = 0x38), made opaque
+  // so that it stays in registers instead of being rebuilt every tile
+  v8i ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = 0x38383838;
+  asm volatile("" : "+v"(ones));
   v4f O[QBW][8], L[QBW], S[QBW][8];
   v8i P[QBW];
   float Mv = -16384.0f, lb[QBW];   // running max per block by row parity (see expcast_tile)
@@ -549,19 +550,19 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
     const float skj = skp[j];
     if (!group_b) {
       expcast_tile<DUMP, EXPP>(S, P, aq8, skj, Mv, O, L, lb, j, j == last_masked, a, g, qrow0);
-      if (VSMOOTH) vsmooth_tile(P, L, lb, s & 3, g);
-      pv_tile<!VSMOOTH, true>(vbuf + b0 * TILE_BYTES, P, O, L, lane, vpre);
+      if (VSMOOTH) vsmooth_tile(P, L, lb, s & 3, g, ones);
+      pv_tile<!VSMOOTH, true>(vbuf + b0 * TILE_BYTES, P, O, L, lane, ones, vpre);
       if (VSMOOTH && ((s & 3) == 3 || s + 1 == nT)) vsmooth_flush(mubuf, s, O, lb, g, l16);
       if (s + 1 < nT) qk_tile(kbuf + b1 * TILE_BYTES, qop, S, lane);
     } else {
       __builtin_amdgcn_s_setprio(2);
       qk_tile(kbuf + b0 * TILE_BYTES, qop, S, lane);
-      if (s > 0) pv_tile<!VSMOOTH>(vbuf + bm1 * TILE_BYTES, P, O, L, lane);
+      if (s > 0) pv_tile<!VSMOOTH>(vbuf + bm1 * TILE_BYTES, P, O, L, lane, ones);
       // the batch that ended with tile s-1 (before ExpCast(s) may rescale)
       if (VSMOOTH && s > 0 && ((s - 1) & 3) == 3) vsmooth_flush(mubuf, s - 1, O, lb, g, l16);
       __builtin_amdgcn_s_setprio(0);
       expcast_tile<DUMP, EXPP>(S, P, aq8, skj, Mv, O, L, lb, j, j == last_masked, a, g, qrow0);
-      if (VSMOOTH) vsmooth_tile(P, L, lb, s & 3, g);
+      if (VSMOOTH) vsmooth_tile(P, L, lb, s & 3, g, ones);
     }
     // group A waits for the loads it issued one iteration ago (a tile is 4
     // loads per thread, plus one for the block means on wave 0 with
@@ -574,7 +575,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   for (; s < nT - 3; ++s) iteration(s, tail_tag<false>{});
   for (; s < nT; ++s) iteration(s, tail_tag<true>{});
   if (group_b) {
-    pv_tile<!VSMOOTH>(vbuf + ((nT - 1) & (NBUF - 1)) * TILE_BYTES, P, O, L, lane);
+    pv_tile<!VSMOOTH>(vbuf + ((nT - 1) & (NBUF - 1)) * TILE_BYTES, P, O, L, lane, ones);
     if (VSMOOTH) vsmooth_flush(mubuf, nT - 1, O, lb, g, l16);
   }
   __builtin_amdgcn_s_waitcnt(0);
