@@ -51,6 +51,12 @@ __device__ inline v4f mfma_f8(const v8i& a, const v8i& b, const v4f& c) {
   // v_mfma_f32_16x16x128_f8f6f4 with A and B as OCP E4M3 (format 0), no block scales
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
+// The same with the B operand's values multiplied by 2^(sb - 127) (E8M0 block
+// scale in byte 0 of sb, per lane, i.e. per column and 32-element K block);
+// the power-of-two factor is exact.
+__device__ inline v4f mfma_f8_sb(const v8i& a, const v8i& b, const v4f& c, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
+}
 
 // The MFMA operand of 16-row block `blk` for this lane: 32 bytes, read as two
 // contiguous 1 KiB wave accesses from an operand-ordered LDS tile
@@ -146,6 +152,38 @@ constexpr int SG_MFMA = 0x008, SG_VALU = 0x002, SG_DS_READ = 0x100;
 // block kb+RA is read while the MFMAs of block kb run
 constexpr int RA = 2;
 
+// largest lag (binades) of the reference max of O and L behind the running max
+constexpr float FRAME_DRIFT = 64.0f;
+
+// c += A B with B's values times 2^(sb - 127), as inline assembly (`one` is a
+// register holding 127, the A operand's unit scale). The PV accumulation uses
+// this form: through the builtin, the register allocator handled its
+// accumulators badly enough to spill (256 VGPRs and about 130 spilled,
+// against 235 and none written out). The compiler does not look inside the
+// statement, so it inserts no wait states for it: every access to c or b by
+// other instructions next to it is separated by hand, with pfence before the
+// first such MFMA of a tile (after the VALU writes of P) and ofence before
+// VALU or another MFMA type touches O. A CPU test scans the compiled kernels
+// for any access that escapes these fences.
+__device__ __forceinline__ void mfma_f8_sb_acc(v4f& c, const v8i& a, const v8i& b, int one, int sb) {
+  asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+               : "+v"(c)
+               : "v"(a), "v"(b), "v"(one), "v"(sb));
+}
+// 4 wait states between the VALU writes of the P operand and the MFMAs that
+// read it (the hardware asks for 2)
+__device__ __forceinline__ void pfence(v8i (&P)[QBW]) {
+  asm volatile("s_nop 3" : "+v"(P[0]), "+v"(P[1]));
+}
+// 24 wait states: more than an 8-pass XDL result needs before VALU reads or
+// overwrites it, or an MFMA of another type accumulates into it
+__device__ __forceinline__ void ofence(v4f (&O)[QBW][8]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+v"(O[0][0]), "+v"(O[0][1]), "+v"(O[0][2]), "+v"(O[0][3]), "+v"(O[0][4]), "+v"(O[0][5]),
+                 "+v"(O[0][6]), "+v"(O[0][7]), "+v"(O[1][0]), "+v"(O[1][1]), "+v"(O[1][2]), "+v"(O[1][3]),
+                 "+v"(O[1][4]), "+v"(O[1][5]), "+v"(O[1][6]), "+v"(O[1][7]));
+}
+
 // S^T = K Q^T for one 128-key tile and the wave's 32 queries, with the K
 // operands read RA blocks ahead, so the LDS latency hides behind 2*RA MFMAs
 // instead of stalling every pair.
@@ -171,8 +209,10 @@ __device__ __forceinline__ void qk_tile(const uint8_t* kt, const v8i (&qop)[QBW]
 // O^T += V^T P^T and (ROWSUM) L += 1 * P^T for one tile, with the same
 // read-ahead. With PRE the first RA operands were read by the caller (pre).
 template <bool ROWSUM = true, bool PRE = false>
-__device__ __forceinline__ void pv_tile(const uint8_t* vt, const v8i (&P)[QBW], v4f (&O)[QBW][8], v4f (&L)[QBW],
-                                        int lane, const v8i& ones, const v8i* pre = nullptr) {
+__device__ __forceinline__ void pv_tile(const uint8_t* vt, v8i (&P)[QBW], const int (&sb)[QBW], int one,
+                                        v4f (&O)[QBW][8], v4f (&L)[QBW], int lane, const v8i& ones,
+                                        const v8i* pre = nullptr) {
+  pfence(P);
   v8i vop[8];
 #pragma unroll
   for (int n = 0; n < RA; ++n) vop[n] = PRE ? pre[n] : lds_operand(vt, n, lane);
@@ -180,11 +220,11 @@ __device__ __forceinline__ void pv_tile(const uint8_t* vt, const v8i (&P)[QBW], 
   for (int n = 0; n < 8; ++n) {
     if (n + RA < 8) vop[n + RA] = lds_operand(vt, n + RA, lane);
 #pragma unroll
-    for (int qb = 0; qb < QBW; ++qb) O[qb][n] = mfma_f8(vop[n], P[qb], O[qb][n]);
+    for (int qb = 0; qb < QBW; ++qb) mfma_f8_sb_acc(O[qb][n], vop[n], P[qb], one, sb[qb]);
   }
   if (ROWSUM) {
 #pragma unroll
-    for (int qb = 0; qb < QBW; ++qb) L[qb] = mfma_f8(ones, P[qb], L[qb]);
+    for (int qb = 0; qb < QBW; ++qb) L[qb] = mfma_f8_sb(ones, P[qb], L[qb], sb[qb]);
   }
   if (!PRE) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2 * RA, 0);
 #pragma unroll
@@ -204,11 +244,11 @@ __device__ __forceinline__ void pv_tile(const uint8_t* vt, const v8i (&P)[QBW], 
 // vsmooth_tile: the row sum l = 1 * P^T (MFMA; every lane gets the sum of its
 // query), L += l, and l goes to the B operand lb of the batch: lanes of group
 // g = slot hold row k = slot (the tile's place in its batch of four).
-__device__ __forceinline__ void vsmooth_tile(const v8i (&P)[QBW], v4f (&L)[QBW], float (&lb)[QBW], int slot, int g,
-                                             const v8i& ones) {
+__device__ __forceinline__ void vsmooth_tile(const v8i (&P)[QBW], const int (&sb)[QBW], v4f (&L)[QBW], float (&lb)[QBW],
+                                             int slot, int g, const v8i& ones) {
 #pragma unroll
   for (int qb = 0; qb < QBW; ++qb) {
-    const v4f l = mfma_f8(ones, P[qb], v4f{0.f, 0.f, 0.f, 0.f});
+    const v4f l = mfma_f8_sb(ones, P[qb], v4f{0.f, 0.f, 0.f, 0.f}, sb[qb]);
     L[qb] += l;
     lb[qb] = g == slot ? l[0] : lb[qb];
   }
@@ -318,17 +358,18 @@ __device__ __forceinline__ void spread_pair(float v, float& v0, float& v1) {
 }
 
 // ExpCast for one tile and the wave's two 16-query blocks: raise the running
-// bit-aligned max (rescaling O and L by the exact power of two when it
-// grows), then one FMA and one saturating convert per score give the E4M3
-// bytes. The running max Mv is kept per block by row parity (rows 0, 2:
+// bit-aligned max (and with it the power-of-two scale that brings the tile's
+// bytes into the frame of O and L), then one FMA per score and one
+// conversion per two scores give the E4M3 bytes. The running max Mv is kept per block by row parity (rows 0, 2:
 // block 0; rows 1, 3: block 1), so that the max, the ceiling, the growth
 // test and the FMA addend take one instruction for both blocks. aq8 is
 // 8*tau*log2(e)*sq/8 for the wave's 32 queries, which share one 128-query
 // scale block.
 template <bool DUMP, bool EXPP>
 __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], float aq8, float skj, float& Mv,
-                                             v4f (&O)[QBW][8], v4f (&L)[QBW], float (&lb)[QBW], int j, bool masked,
-                                             const AttnArgs& a, int g, int qrow0) {
+                                             float& Mr, int (&sb)[QBW], v4f (&O)[QBW][8], v4f (&L)[QBW],
+                                             float (&lb)[QBW], int j, bool masked, const AttnArgs& a, int g,
+                                             int qrow0) {
   if (masked) {
     // keys beyond S in the last (ragged) tile take no part in max or sums.
     // The empty asm makes lim opaque, so that the 32 compares stay in this
@@ -351,19 +392,35 @@ __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], fl
   const float mv = row_max_pair(lane_max32(S[0]), lane_max32(S[1]));
   const float Mn = fmax_p(Mv, __builtin_ceilf(aqs8 * mv));
   if (__builtin_amdgcn_ballot_w64(Mn > Mv) != 0) {
-    float d0, d1;   // exponent change of each block (<= 0)
-    spread_pair(Mv - Mn, d0, d1);
-    const int d[QBW] = {(int)d0, (int)d1};
+    // O and L stay in the frame of a reference max Mr <= M: the bytes of this
+    // tile weigh 2^(Mn - Mr) there, a factor the PV and row-sum MFMAs apply as
+    // the E8M0 scale of their P operand. O and L are rescaled (exactly, by a
+    // power of two) only where the frame would fall more than FRAME_DRIFT
+    // binades behind, which includes the first tile.
+    float e = Mn - Mr;
+    if (__builtin_amdgcn_ballot_w64(e > FRAME_DRIFT) != 0) {
+      ofence(O);
+      const bool re = e > FRAME_DRIFT;
+      float d0, d1;   // exponent change of each block (<= 0)
+      spread_pair(re ? -e : 0.0f, d0, d1);
+      const int d[QBW] = {(int)d0, (int)d1};
 #pragma unroll
-    for (int qb = 0; qb < QBW; ++qb) {
+      for (int qb = 0; qb < QBW; ++qb) {
 #pragma unroll
-      for (int n = 0; n < 8; ++n)
+        for (int n = 0; n < 8; ++n)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) O[qb][n][r] = __builtin_ldexpf(O[qb][n][r], d[qb]);
+          for (int r = 0; r < 4; ++r) O[qb][n][r] = __builtin_ldexpf(O[qb][n][r], d[qb]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) L[qb][r] = __builtin_ldexpf(L[qb][r], d[qb]);
-      lb[qb] = __builtin_ldexpf(lb[qb], d[qb]);   // V-Smooth row sums not yet added
+        for (int r = 0; r < 4; ++r) L[qb][r] = __builtin_ldexpf(L[qb][r], d[qb]);
+        lb[qb] = __builtin_ldexpf(lb[qb], d[qb]);   // V-Smooth row sums not yet added
+      }
+      Mr = re ? Mn : Mr;
+      e = re ? 0.0f : e;
     }
+    float e0, e1;
+    spread_pair(e, e0, e1);
+    sb[0] = 127 + (int)e0;
+    sb[1] = 127 + (int)e1;
     Mv = Mn;
   }
   float b[QBW];   // the FMA's addend per block, in every lane
@@ -495,6 +552,10 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   v4f O[QBW][8], L[QBW], S[QBW][8];
   v8i P[QBW];
   float Mv = -16384.0f, lb[QBW];   // running max per block by row parity (see expcast_tile)
+  float Mr = -16384.0f;            // reference max of O and L, same layout
+  int sb[QBW] = {127, 127};        // E8M0 scale of the P operand: 2^(M - Mr)
+  int one = 127;                   // the V operand's unit scale, in a register
+  asm volatile("" : "+v"(one));
   const float aq8 = aq[0] * 0.125f;
 #pragma unroll
   for (int qb = 0; qb < QBW; ++qb) {
@@ -556,20 +617,20 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
     if (ld_mu) load_means(mofs + ((s + 2) & (MU_NBUF - 1)) * MU_SLOT, mu_ptr(s + 2), voff_mu);
     const float skj = skp[j];
     if (!group_b) {
-      expcast_tile<DUMP, EXPP>(S, P, aq8, skj, Mv, O, L, lb, j, j == last_masked, a, g, qrow0);
-      if (VSMOOTH) vsmooth_tile(P, L, lb, s & 3, g, ones);
-      pv_tile<!VSMOOTH, true>(vbuf + b0 * TILE_BYTES, P, O, L, lane, ones, vpre);
-      if (VSMOOTH && ((s & 3) == 3 || s + 1 == nT)) vsmooth_flush(mubuf, s, O, lb, g, l16);
+      expcast_tile<DUMP, EXPP>(S, P, aq8, skj, Mv, Mr, sb, O, L, lb, j, j == last_masked, a, g, qrow0);
+      if (VSMOOTH) vsmooth_tile(P, sb, L, lb, s & 3, g, ones);
+      pv_tile<!VSMOOTH, true>(vbuf + b0 * TILE_BYTES, P, sb, one, O, L, lane, ones, vpre);
+      if (VSMOOTH && ((s & 3) == 3 || s + 1 == nT)) { ofence(O); vsmooth_flush(mubuf, s, O, lb, g, l16); }
       if (s + 1 < nT) qk_tile(kbuf + b1 * TILE_BYTES, qop, S, lane);
     } else {
       __builtin_amdgcn_s_setprio(2);
       qk_tile(kbuf + b0 * TILE_BYTES, qop, S, lane);
-      if (s > 0) pv_tile<!VSMOOTH>(vbuf + bm1 * TILE_BYTES, P, O, L, lane, ones);
+      if (s > 0) pv_tile<!VSMOOTH>(vbuf + bm1 * TILE_BYTES, P, sb, one, O, L, lane, ones);
       // the batch that ended with tile s-1 (before ExpCast(s) may rescale)
-      if (VSMOOTH && s > 0 && ((s - 1) & 3) == 3) vsmooth_flush(mubuf, s - 1, O, lb, g, l16);
+      if (VSMOOTH && s > 0 && ((s - 1) & 3) == 3) { ofence(O); vsmooth_flush(mubuf, s - 1, O, lb, g, l16); }
       __builtin_amdgcn_s_setprio(0);
-      expcast_tile<DUMP, EXPP>(S, P, aq8, skj, Mv, O, L, lb, j, j == last_masked, a, g, qrow0);
-      if (VSMOOTH) vsmooth_tile(P, L, lb, s & 3, g, ones);
+      expcast_tile<DUMP, EXPP>(S, P, aq8, skj, Mv, Mr, sb, O, L, lb, j, j == last_masked, a, g, qrow0);
+      if (VSMOOTH) vsmooth_tile(P, sb, L, lb, s & 3, g, ones);
     }
     // group A waits for the loads it issued one iteration ago (a tile is 4
     // loads per thread, plus one for the block means on wave 0 with
@@ -582,8 +643,27 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   for (; s < nT - 3; ++s) iteration(s, tail_tag<false>{});
   for (; s < nT; ++s) iteration(s, tail_tag<true>{});
   if (group_b) {
-    pv_tile<!VSMOOTH>(vbuf + ((nT - 1) & (NBUF - 1)) * TILE_BYTES, P, O, L, lane, ones);
-    if (VSMOOTH) vsmooth_flush(mubuf, nT - 1, O, lb, g, l16);
+    pv_tile<!VSMOOTH>(vbuf + ((nT - 1) & (NBUF - 1)) * TILE_BYTES, P, sb, one, O, L, lane, ones);
+    if (VSMOOTH) {
+      ofence(O);
+      vsmooth_flush(mubuf, nT - 1, O, lb, g, l16);
+    }
+  }
+  {
+    // O and L from the reference frame to the final running max (exact)
+    ofence(O);
+    float d0, d1;
+    spread_pair(Mr - Mv, d0, d1);
+    const int d[QBW] = {(int)d0, (int)d1};
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb) {
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) O[qb][n][r] = __builtin_ldexpf(O[qb][n][r], d[qb]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) L[qb][r] = __builtin_ldexpf(L[qb][r], d[qb]);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
 
