@@ -3,7 +3,8 @@
 * ExpCast bytes: the kernel's own bytes (debug dump) against the oracle's
   bytes for the same logits and the running row max the kernel used: at
   least 99.9% equal, never more than one code apart (the remaining
-  differences come from fp32 scores and FMA against float64 in the oracle).
+  differences come from the kernel's logits, summed by the FP8 MFMA and
+  scaled in fp32, against float64 in the oracle).
 * Output: relative L2 against the oracle <= 5e-3, at every workload size
   (all rows on the small ones, sampled rows, always including the ragged tail,
   on the large ones, in the launch configuration the benchmark times).
@@ -33,21 +34,28 @@ def _oc():
 
 
 def logit_error_bound(ph, rows, tau):
-    """Worst-case difference between the kernel's fp32 logit and the exact
-    one: the MFMA sums 128 FP8 products in fp32 (error at most 128 * 2^-24 *
-    sum |products|), then three fp32 scale products and the FMA round
-    (a few ulp of the logit)."""
-    qa = np.abs(oracle.decode(ph.qc[np.asarray(rows)]))
-    ka = np.abs(oracle.decode(ph.kc))
+    """Worst-case difference between the kernel's logit and the exact one.
+    The FP8 MFMA does not sum its 128 products to fp32 accuracy: measured on
+    gfx950 against exact sums (8192 trials of random codes, and of small
+    codes beside one dominant product), its error stayed within 2^-11.3 of
+    the largest product's magnitude; the bound allows 2^-10 of the largest
+    possible product, max|q| * max|k|. On top of that, fp32 rounding of the
+    sum (128 * 2^-24 * sum |products|) and of the three scale products and
+    the FMA (a few ulp of the logit)."""
+    qd = np.abs(oracle.decode(ph.qc[np.asarray(rows)]))
+    kd = np.abs(oracle.decode(ph.kc))
     sqr = ph.sq[np.asarray(rows) // 128].astype(np.float64)
     skk = ph.sk[np.arange(ph.S) // 128].astype(np.float64)
-    mag = (tau / math.log(2)) * (qa @ ka.T) * (sqr[:, None] * skk[None, :])
-    return mag * (128 * 2.0 ** -24) + mag * 2.0 ** -20
+    scale = (tau / math.log(2)) * (sqr[:, None] * skk[None, :])
+    mag = scale * (qd @ kd.T)
+    top = scale * np.outer(qd.max(axis=1), kd.max(axis=1))
+    return mag * (128 * 2.0 ** -24) + mag * 2.0 ** -20 + top * 2.0 ** -10
 
 
 def check_max_trace(kernel_trace, own, x, bound, order="mid"):
     """The kernel's running max per tile must match the oracle's, except where
-    a tile's largest logit lies within the fp32 error bound of an integer:
+    a tile's largest logit lies within the kernel's logit error bound of an
+    integer:
     there the first divergence must be exactly one, at such a tie."""
     nT = kernel_trace.shape[1]
     tiles = oracle.key_tile_order(nT) if order == "mid" else list(range(nT))
@@ -129,7 +137,7 @@ def test_expcast_bytes_match_oracle(case):
             log(f"  (b={b},h={h}) byte agreement {agree:.6f}, max diff {diff.max()}")
             assert agree >= 0.999 and diff.max() <= 1
             # the final running max is the bit-aligned row max, except where the
-            # row's largest logit lies within the fp32 error bound of an integer
+            # row's largest logit lies within the logit error bound of an integer
             Mfinal = m_used.max(axis=1)
             Mo = oracle.bitaligned_row_max(x)
             bad = np.nonzero(Mfinal != Mo)[0]
@@ -200,6 +208,34 @@ def test_identical_keys_give_mean_value():
     mean = float(ph.sv) * oracle.decode(ph.vc).mean(axis=0)
     got = out[0, :, 0].float().cpu().numpy()
     assert oracle.rel_l2(got, np.tile(mean, (S, 1))) < 4e-3
+
+
+def test_running_max_rising_by_many_binades():
+    """The kernel keeps O and L in the frame of a reference max and re-anchors
+    them (by an exact power of two) once the running max has risen more than
+    64 binades past it. Here the first 16 queries of every 32 see their max
+    rise by about 41 binades at each key tile they visit: those queries hold
+    2 in channels 0-63 and the keys of the i-th visited tile 2.5*i there, so
+    their frame is re-anchored with O and L already non-zero, while the other
+    16 queries of the same waves behave normally. (The large logit is spread
+    over 64 equal products: a single dominant product would instead test the
+    FP8 MFMA's summation precision, which is coarser than fp32.)"""
+    oc = _oc()
+    S = 1024
+    g = torch.Generator().manual_seed(31)
+    q = torch.randn(1, S, 1, 128, generator=g) * 0.5
+    k = torch.randn(1, S, 1, 128, generator=g) * 0.5
+    v = torch.randn(1, S, 1, 128, generator=g)
+    rising = torch.as_tensor((np.arange(S) % 32) < 16)
+    q[0, rising, 0, :64] = 2.0
+    for i, t in enumerate(oracle.key_tile_order(S // 128)):
+        k[0, 128 * t:128 * (t + 1), 0, :64] = 2.5 * i
+    q, k, v = (x.to(torch.bfloat16).cuda() for x in (q, k, v))
+    prep = oc.prepare(q, k, v)
+    out = oc.attention(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    _compare(q, k, v, out, [(0, 0)], np.arange(S), label="rising max", prep=prep)
 
 
 def test_three_dim_and_strided_inputs():
