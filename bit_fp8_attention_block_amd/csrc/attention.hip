@@ -6,19 +6,22 @@
 // evaluated and no FP32->FP8 conversion is made. With a = 8*tau*log2(e)*sq*sk
 // for the (query block, key tile) pair and the bit-aligned running row max M,
 //     byte = clamp(rne(a*s_raw + (119.65 - 8*M)), 0, 255)
-// is one v_fma_f32 and one v_cvt_pk_u8_f32 (which rounds to nearest even and
-// clamps). The byte never exceeds 120 because M >= ceil(a*s_raw/8), and
-// scores more than ~15 binades below the max land on 0.
+// is one v_fma_f32 per score and one v_cvt_pknorm_u16_f32 per two scores
+// (rounding to nearest, clamping), plus a byte permute per four. The byte
+// never exceeds 120 because M >= ceil(a*s_raw/8), and scores more than ~15
+// binades below the max land on 0.
 //
 // For comparison the same kernel can instead take the path ExpCast replaces
 // (weights selection OC_WEIGHTS_EXP_FP8): weight 256*2^(x - M) from v_exp_f32,
 // then the hardware FP32 -> E4M3 cast (v_cvt_pk_fp8_f32), with everything else
-// (max, rescale, sums, MFMAs) unchanged.
+// (max, frame scale, sums, MFMAs) unchanged.
 //
 // Because M is an integer, the weights of earlier tiles relative to a stale M
-// differ from those relative to the new M by an exact power of two. The
-// rescale is then an exact v_ldexp on O and L, and the result does not depend
-// on the key-tile order (up to the underflow tail).
+// differ from those relative to the new M by an exact power of two. O and L
+// are kept in the frame of a reference max, and each tile's weights enter it
+// through that power of two as the E8M0 scale of the PV MFMA's P operand, so
+// growth of M costs no rescale of O and L; the result does not depend on the
+// key-tile order (up to the underflow tail).
 //
 // Layout of the work (one workgroup = 256 queries of one (b, h)):
 //  * S^T = K Q^T on v_mfma_f32_16x16x128_f8f6f4. Lane l then holds keys
@@ -626,7 +629,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
       __builtin_amdgcn_s_setprio(2);
       qk_tile(kbuf + b0 * TILE_BYTES, qop, S, lane);
       if (s > 0) pv_tile<!VSMOOTH>(vbuf + bm1 * TILE_BYTES, P, sb, one, O, L, lane, ones);
-      // the batch that ended with tile s-1 (before ExpCast(s) may rescale)
+      // the batch that ended with tile s-1 (before ExpCast(s) may re-anchor)
       if (VSMOOTH && s > 0 && ((s - 1) & 3) == 3) { ofence(O); vsmooth_flush(mubuf, s - 1, O, lb, g, l16); }
       __builtin_amdgcn_s_setprio(0);
       expcast_tile<DUMP, EXPP>(S, P, aq8, skj, Mv, Mr, sb, O, L, lb, j, j == last_masked, a, g, qrow0);

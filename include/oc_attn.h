@@ -155,7 +155,7 @@ void oc_attn_plan_destroy(oc_attn_plan* plan);
  *     exponential, then an FP32->FP8 cast). Weight 256*2^(x - M) from one
  *     v_exp_f32 per score (within 1 ulp of the rounded value), then the
  *     hardware FP32->E4M3 cast, round-to-nearest-even. The running max,
- *     rescales, row sums, MFMAs and repair are unchanged.
+ *     its power-of-two scaling, row sums, MFMAs and repair are unchanged.
  * Any other value gives OC_ERR_INVALID_ARGUMENT and leaves the plan as it
  * was. */
 typedef enum oc_weights { OC_WEIGHTS_EXPCAST = 0, OC_WEIGHTS_EXP_FP8 = 1 } oc_weights;
