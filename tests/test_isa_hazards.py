@@ -4,7 +4,7 @@ The PV accumulation is issued as inline assembly (a scaled FP8 MFMA), which
 the compiler does not look into: it inserts no wait states between that
 instruction and the VALU code around it. The kernel separates them by hand.
 This test compiles the kernels for gfx950 and checks every instantiation's
-machine code, following branches:
+machine code, following branches (accumulators may be VGPRs or AGPRs):
   - after an inline-assembly MFMA, no other instruction reads or writes its
     accumulator registers within AFTER wait states (an 8-pass XDL result
     needs 12 before VALU may read it; 24 are given),
@@ -37,12 +37,13 @@ def _build_module():
 
 
 def _regs(text):
+    """VGPRs and AGPRs named in an operand list, as ('v', n) / ('a', n)."""
     out = set()
-    for m in re.finditer(r"\bv\[(\d+):(\d+)\]|\bv(\d+)\b", text):
-        if m.group(3):
-            out.add(int(m.group(3)))
+    for m in re.finditer(r"\b([va])\[(\d+):(\d+)\]|\b([va])(\d+)\b", text):
+        if m.group(4):
+            out.add((m.group(4), int(m.group(5))))
         else:
-            out.update(range(int(m.group(1)), int(m.group(2)) + 1))
+            out.update((m.group(1), r) for r in range(int(m.group(2)), int(m.group(3)) + 1))
     return out
 
 
@@ -119,7 +120,7 @@ def scan(body):
 
 
 def _functions(asm):
-    for m in re.finditer(r"^(_ZN2oc11attn_kernel\w+):", asm, re.M):
+    for m in re.finditer(r"^(_ZN2oc1\d+attn_kernel\w*):", asm, re.M):
         end = asm.index(".Lfunc_end", m.end())
         yield m.group(1), asm[m.end():end]
 
