@@ -210,7 +210,8 @@ def test_identical_keys_give_mean_value():
     assert oracle.rel_l2(got, np.tile(mean, (S, 1))) < 4e-3
 
 
-def test_running_max_rising_by_many_binades():
+@pytest.mark.parametrize("variant", ["expcast", "exp_fp8", "repair"])
+def test_running_max_rising_by_many_binades(variant):
     """The kernel keeps O and L in the frame of a reference max and re-anchors
     them (by an exact power of two) once the running max has risen more than
     64 binades past it. Here the first 16 queries of every 32 see their max
@@ -231,11 +232,18 @@ def test_running_max_rising_by_many_binades():
     for i, t in enumerate(oracle.key_tile_order(S // 128)):
         k[0, 128 * t:128 * (t + 1), 0, :64] = 2.5 * i
     q, k, v = (x.to(torch.bfloat16).cuda() for x in (q, k, v))
-    prep = oc.prepare(q, k, v)
-    out = oc.attention(q, k, v)
+    log(f"[rising max] variant={variant}")
+    if variant == "repair":
+        prep = oc.prepare_v_repair(q, k, v, 0.02)
+        out = oc.attention_v_repair(q, k, v, 0.02)
+        opts = dict(budget=0.02)
+    else:
+        prep = oc.prepare(q, k, v)
+        out = oc.attention(q, k, v, weights=variant)
+        opts = dict(weights="exp_cast" if variant == "exp_fp8" else "expcast")
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
-    _compare(q, k, v, out, [(0, 0)], np.arange(S), label="rising max", prep=prep)
+    _compare(q, k, v, out, [(0, 0)], np.arange(S), label=f"rising max ({variant})", prep=prep, **opts)
 
 
 def test_three_dim_and_strided_inputs():
