@@ -420,9 +420,10 @@ __global__ __launch_bounds__(1024) void select_kernel(PrepArgs a) {
   const int S = a.S, k = a.n_sel;
   const uint64_t* e = reinterpret_cast<const uint64_t*>(a.energy + (int64_t)bh * S);
   __shared__ uint32_t hist[256];
+  __shared__ uint32_t above[256];   // tokens in higher bins, by bin
   __shared__ int scratch[16];
   __shared__ uint64_t s_prefix;
-  __shared__ int s_krem;
+  __shared__ int s_krem, s_all;
   __shared__ float red[16];
 
   uint64_t prefix = 0, mask = 0;
@@ -456,21 +457,38 @@ __global__ __launch_bounds__(1024) void select_kernel(PrepArgs a) {
     }
     if (run) atomicAdd(&hist[run_bin], run);
     __syncthreads();
-    if (tid == 0) {
-      int cum = 0, bin = 255;
-      for (; bin > 0; --bin) {
-        if (cum + (int)hist[bin] >= krem) break;
-        cum += (int)hist[bin];
+    // the bin of the krem-th largest: above[b] = tokens in bins > b (an
+    // inclusive suffix scan over the 256 bins, 8 steps), then the one bin with
+    // above[b] < krem <= above[b] + hist[b]
+    if (tid < 256) above[tid] = hist[tid];
+    __syncthreads();
+#pragma unroll
+    for (int d = 1; d < 256; d <<= 1) {
+      const uint32_t add = tid < 256 && tid + d < 256 ? above[tid + d] : 0u;
+      __syncthreads();
+      if (tid < 256) above[tid] += add;
+      __syncthreads();
+    }
+    if (tid < 256) {
+      const int gt = (int)(above[tid] - hist[tid]);
+      if (gt < krem && krem <= (int)above[tid]) {
+        s_prefix = prefix | ((uint64_t)tid << shift);
+        s_krem = krem - gt;
+        s_all = (int)hist[tid] == krem - gt;
       }
-      s_prefix = prefix | ((uint64_t)bin << shift);
-      s_krem = krem - cum;
     }
     __syncthreads();
     prefix = s_prefix;
     krem = s_krem;
     mask |= (uint64_t)255 << shift;
+    // every token whose leading bits equal the prefix is taken: the set is
+    // settled, and finer digits would not change it
+    if (s_all) break;
+    __syncthreads();
   }
-  // prefix = bits of the k-th largest energy T; krem = how many tokens equal to T to take
+  // prefix = the leading bits (under mask) of the k-th largest energy T;
+  // krem = how many tokens with those bits to take (all of them when the
+  // passes stopped early)
   const int chunk = (S + 1023) / 1024;
   const int i0 = min(S, tid * chunk), i1 = min(S, i0 + chunk);
   int gt = 0, eq = 0;
@@ -480,8 +498,8 @@ __global__ __launch_bounds__(1024) void select_kernel(PrepArgs a) {
     for (int j = 0; j < 8; ++j) u[j] = ib + j < i1 ? e[ib + j] : 0u;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      gt += ib + j < i1 && u[j] > prefix;
-      eq += ib + j < i1 && u[j] == prefix;
+      gt += ib + j < i1 && (u[j] & mask) > prefix;
+      eq += ib + j < i1 && (u[j] & mask) == prefix;
     }
   }
   int tot;
@@ -497,9 +515,10 @@ __global__ __launch_bounds__(1024) void select_kernel(PrepArgs a) {
       for (int j = 0; j < 8; ++j) u[j] = ib + j < i1 ? e[ib + j] : 0u;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        if (ib + j < i1 && (u[j] > prefix || (u[j] == prefix && taken < take_eq))) {
+        const uint64_t um = u[j] & mask;
+        if (ib + j < i1 && (um > prefix || (um == prefix && taken < take_eq))) {
           sel[pos++] = ib + j;
-          if (u[j] == prefix) ++taken;
+          if (um == prefix) ++taken;
         }
       }
     }
