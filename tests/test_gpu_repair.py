@@ -46,6 +46,45 @@ def test_repair_set_bit_exact(S, H, budget):
         assert np.array_equal(sks[:kk], ph.sk[rp.sel // 128]) and not sks[kk:].any()
 
 
+def _tied_values(pattern, S, H):
+    """Values whose residual energies tie: all zero (every value exact in
+    E4M3), or a few rows repeated with a period, so that groups of equal
+    energy straddle the cut."""
+    g = torch.Generator().manual_seed(11)
+    if pattern == "all_zero_energy":
+        v = torch.zeros(1, S, H, 128)
+        v[..., 0] = 1.0
+        v[:, ::3, :, 1] = -0.5
+    else:
+        period = 7 if pattern == "period7" else 97
+        base = torch.randn(period, H, 128, generator=g)
+        v = base[torch.arange(S) % period].unsqueeze(0)
+    return v.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("pattern,budget", [("all_zero_energy", 0.05), ("period7", 0.05), ("period7", 0.2),
+                                            ("period97", 0.3)])
+def test_repair_set_with_tied_energies(pattern, budget):
+    """Equal energies go to the lower token index, also where the cut falls
+    inside a group of equal energies."""
+    oc = _oc()
+    S, H = 1000, 2
+    log(f"[repair ties] {pattern} budget={budget}")
+    q, k, _ = workloads.make_inputs("s8192_h8", device="cuda", S=S, H=H)
+    v = _tied_values(pattern, S, H).to("cuda")
+    prep = oc.prepare_v_repair(q, k, v, budget)
+    torch.cuda.synchronize()
+    w = WsView(prep)
+    kk = oracle.repair_count(budget, S)
+    for h in range(H):
+        rp = oracle.prepare_head(head64(q, 0, h), head64(k, 0, h), head64(v, 0, h), budget).repair
+        assert len(np.unique(rp.energy)) < S // 5   # the ties are real
+        np.testing.assert_allclose(w.energy(0, h), rp.energy, rtol=1e-14, atol=0)
+        assert np.array_equal(w.sel(0, h, kk), rp.sel), (h, "selected tokens")
+        assert w.sr(0, h)[0] == rp.sr, (h, "residual scale")
+        assert np.array_equal(w.rcodes(0, h, kk), rp.rc), (h, "residual codes")
+
+
 @pytest.mark.parametrize("name,budget,rows_per_head,pairs", [
     ("s8192_h8", 0.005, 512, [(0, 0), (0, 3), (0, 7)]),
     ("s8192_h8", 0.05, 256, [(0, 1), (0, 6)]),
