@@ -154,6 +154,8 @@ constexpr int SG_MFMA = 0x008, SG_VALU = 0x002, SG_DS_READ = 0x100;
 // LDS operand read-ahead of the tile loops, in 16-row blocks: the operand of
 // block kb+RA is read while the MFMAs of block kb run
 constexpr int RA = 2;
+// K operands of its next QK that group B reads before each barrier
+constexpr int KPRE = 2;
 
 // largest lag (binades) of the reference max of O and L behind the running max
 constexpr float FRAME_DRIFT = 64.0f;
@@ -189,22 +191,26 @@ __device__ __forceinline__ void ofence(v4f (&O)[QBW][8]) {
 
 // S^T = K Q^T for one 128-key tile and the wave's 32 queries, with the K
 // operands read RA blocks ahead, so the LDS latency hides behind 2*RA MFMAs
-// instead of stalling every pair.
-__device__ __forceinline__ void qk_tile(const uint8_t* kt, const v8i (&qop)[QBW], v4f (&S)[QBW][8], int lane) {
+// instead of stalling every pair. The first NPRE (0 or >= RA) operands were
+// read by the caller (pre).
+template <int NPRE = 0>
+__device__ __forceinline__ void qk_tile(const uint8_t* kt, const v8i (&qop)[QBW], v4f (&S)[QBW][8], int lane,
+                                        const v8i* pre = nullptr) {
+  static_assert(NPRE == 0 || (NPRE >= RA && NPRE <= 8), "read-ahead");
   v8i kop[8];
 #pragma unroll
-  for (int kb = 0; kb < RA; ++kb) kop[kb] = lds_operand(kt, kb, lane);
+  for (int kb = 0; kb < (NPRE ? NPRE : RA); ++kb) kop[kb] = NPRE ? pre[kb] : lds_operand(kt, kb, lane);
 #pragma unroll
   for (int kb = 0; kb < 8; ++kb) {
-    if (kb + RA < 8) kop[kb + RA] = lds_operand(kt, kb + RA, lane);
+    if (kb + RA < 8 && kb + RA >= NPRE) kop[kb + RA] = lds_operand(kt, kb + RA, lane);
 #pragma unroll
     for (int qb = 0; qb < QBW; ++qb) S[qb][kb] = mfma_f8(kop[kb], qop[qb], v4f{0.f, 0.f, 0.f, 0.f});
   }
-  __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2 * RA, 0);
+  if (!NPRE) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2 * RA, 0);
 #pragma unroll
   for (int kb = 0; kb < 8 - RA; ++kb) {
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, QBW, 0);
-    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+    if (kb + RA >= NPRE) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
   }
   __builtin_amdgcn_sched_group_barrier(SG_MFMA, RA * QBW, 0);
 }
@@ -463,7 +469,7 @@ __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], fl
 
 // the two parts of the tile loop (see the kernel)
 template <bool V>
-struct tail_tag {
+struct bool_tag {
   static constexpr bool value = V;
 };
 
@@ -491,6 +497,9 @@ __device__ __forceinline__ void wait_loads(bool all, bool ld_k, bool ld_v, bool 
 // (group A reads its first PV operands before the ExpCast, so that its MFMA
 // phase starts without an LDS wait)
 //   group B, iteration s:  QK(s), PV(s-1)    | ExpCast(s)
+// (group B reads the first operands of QK(s+1) and PV(s) after its ExpCast,
+// before the barrier; the two groups run separate copies of the loop, so
+// group B holds no scores across it and has the registers for them)
 // Group B starts its MFMAs right after the barrier, at raised priority, so
 // the partner wave's MFMAs do not interleave with them and delay B's ExpCast.
 // Only group A issues the tile loads (issuing the 32 KiB of one iteration
@@ -597,56 +606,79 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   __builtin_amdgcn_s_waitcnt(0);   // this wave's chunks are in LDS
   __syncthreads();
   if (!group_b) qk_tile(kbuf, qop, S, lane);
-  v8i vpre[RA];   // group A: first V operands of its PV, read before its ExpCast
+  // first operands read ahead of their MFMAs, so those start without an LDS
+  // wait. pre: group A, V operands of its PV, read before its ExpCast;
+  // group B, K operands of its next QK. bpre: group B, V operands of its next
+  // PV. Group B reads both before the barrier that ends an iteration.
+  v8i pre[KPRE > RA ? KPRE : RA];
+  v8i bpre[RA];
 
   // One iteration of the tile loop. Before the last three steps (TAIL
   // false) every tile load is issued, so the load flags are constants.
-  const auto iteration = [&](int s, auto tail) {
+  const auto iteration = [&](int s, auto tail, auto grp) {
     constexpr bool TAIL = decltype(tail)::value;
+    constexpr bool GB = decltype(grp)::value;   // group B
     const int j = tile_at(s, centre, nT, a.order);
     const int b0 = s & (NBUF - 1), b1 = (s + 1) & (NBUF - 1), bm1 = (s - 1) & (NBUF - 1);
     const bool ld_k = !TAIL || s + 3 < nT, ld_v = !TAIL || s + 2 < nT;
-    if (!group_b) {
+    if (!GB) {
       // V tile s is in LDS since the last barrier: its first operands arrive
       // while the ExpCast below runs, so the PV MFMAs start without waiting
 #pragma unroll
-      for (int i = 0; i < RA; ++i) vpre[i] = lds_operand(vbuf + b0 * TILE_BYTES, i, lane);
+      for (int i = 0; i < RA; ++i) pre[i] = lds_operand(vbuf + b0 * TILE_BYTES, i, lane);
     }
     // (group A is waves 0-3, threads 0-255)
-    if (ld_k && !group_b) load_tile<NTHREADS / 2>(kofs + ((s + 3) & (NBUF - 1)) * TILE_BYTES, kt_ptr(s + 3), voff, wvs);
-    if (ld_v && !group_b) load_tile<NTHREADS / 2>(vofs + ((s + 2) & (NBUF - 1)) * TILE_BYTES, vt_ptr(s + 2), voff, wvs);
+    if (ld_k && !GB) load_tile<NTHREADS / 2>(kofs + ((s + 3) & (NBUF - 1)) * TILE_BYTES, kt_ptr(s + 3), voff, wvs);
+    if (ld_v && !GB) load_tile<NTHREADS / 2>(vofs + ((s + 2) & (NBUF - 1)) * TILE_BYTES, vt_ptr(s + 2), voff, wvs);
     // V-Smooth: one more 1 KiB load on wave 0, the block means of tile s+2
     const bool ld_mu = VSMOOTH && ld_v && wv == 0;
     if (ld_mu) load_means(mofs + ((s + 2) & (MU_NBUF - 1)) * MU_SLOT, mu_ptr(s + 2), voff_mu);
     const float skj = skp[j];
-    if (!group_b) {
+    if (!GB) {
       expcast_tile<DUMP, EXPP>(S, P, aq8, skj, Mv, Mr, sb, O, L, lb, j, j == last_masked, a, g, qrow0);
       if (VSMOOTH) vsmooth_tile(P, sb, L, lb, s & 3, g, ones);
-      pv_tile<!VSMOOTH, true>(vbuf + b0 * TILE_BYTES, P, sb, one, O, L, lane, ones, vpre);
+      pv_tile<!VSMOOTH, true>(vbuf + b0 * TILE_BYTES, P, sb, one, O, L, lane, ones, pre);
       if (VSMOOTH && ((s & 3) == 3 || s + 1 == nT)) { ofence(O); vsmooth_flush(mubuf, s, O, lb, g, l16); }
       if (s + 1 < nT) qk_tile(kbuf + b1 * TILE_BYTES, qop, S, lane);
     } else {
       __builtin_amdgcn_s_setprio(2);
-      qk_tile(kbuf + b0 * TILE_BYTES, qop, S, lane);
-      if (s > 0) pv_tile<!VSMOOTH>(vbuf + bm1 * TILE_BYTES, P, sb, one, O, L, lane, ones);
+      qk_tile<KPRE>(kbuf + b0 * TILE_BYTES, qop, S, lane, pre);
+      if (s > 0) pv_tile<!VSMOOTH, true>(vbuf + bm1 * TILE_BYTES, P, sb, one, O, L, lane, ones, bpre);
       // the batch that ended with tile s-1 (before ExpCast(s) may re-anchor)
       if (VSMOOTH && s > 0 && ((s - 1) & 3) == 3) { ofence(O); vsmooth_flush(mubuf, s - 1, O, lb, g, l16); }
       __builtin_amdgcn_s_setprio(0);
       expcast_tile<DUMP, EXPP>(S, P, aq8, skj, Mv, Mr, sb, O, L, lb, j, j == last_masked, a, g, qrow0);
       if (VSMOOTH) vsmooth_tile(P, sb, L, lb, s & 3, g, ones);
+      // K step s+1 and V step s have been in LDS since the last barrier: the
+      // first operands of the next QK and PV arrive before the next one
+      if (s + 1 < nT) {
+#pragma unroll
+        for (int i = 0; i < KPRE; ++i) pre[i] = lds_operand(kbuf + b1 * TILE_BYTES, i, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < RA; ++i) bpre[i] = lds_operand(vbuf + b0 * TILE_BYTES, i, lane);
     }
     // group A waits for the loads it issued one iteration ago (a tile is 4
     // loads per thread, plus one for the block means on wave 0 with
     // V-Smooth); this iteration's stay in flight. The code dump's stores also
     // count, so that path drains everything.
-    wait_loads(DUMP || group_b, ld_k, ld_v, ld_mu);
+    wait_loads(DUMP || GB, ld_k, ld_v, ld_mu);
     lds_barrier();
   };
+  // one loop per group, so that each keeps only its own values live across
+  // the back edge (group B holds no scores there, group A no weights)
   int s = 0;
-  for (; s < nT - 3; ++s) iteration(s, tail_tag<false>{});
-  for (; s < nT; ++s) iteration(s, tail_tag<true>{});
   if (group_b) {
-    pv_tile<!VSMOOTH>(vbuf + ((nT - 1) & (NBUF - 1)) * TILE_BYTES, P, sb, one, O, L, lane, ones);
+#pragma unroll
+    for (int i = 0; i < KPRE; ++i) pre[i] = lds_operand(kbuf, i, lane);   // K step 0 is in buffer 0
+    for (; s < nT - 3; ++s) iteration(s, bool_tag<false>{}, bool_tag<true>{});
+    for (; s < nT; ++s) iteration(s, bool_tag<true>{}, bool_tag<true>{});
+  } else {
+    for (; s < nT - 3; ++s) iteration(s, bool_tag<false>{}, bool_tag<false>{});
+    for (; s < nT; ++s) iteration(s, bool_tag<true>{}, bool_tag<false>{});
+  }
+  if (group_b) {
+    pv_tile<!VSMOOTH, true>(vbuf + ((nT - 1) & (NBUF - 1)) * TILE_BYTES, P, sb, one, O, L, lane, ones, bpre);
     if (VSMOOTH) {
       ofence(O);
       vsmooth_flush(mubuf, nT - 1, O, lb, g, l16);
