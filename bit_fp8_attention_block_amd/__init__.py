@@ -47,7 +47,7 @@ class Desc(ctypes.Structure):
 
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in ("qhat", "kpack", "vpack", "sq", "sk", "vamax", "sv", "energy", "sel",
-                                               "kselpack", "rpack", "sksel", "sr", "kmean", "kpart", "vmu", "vmus",
+                                               "kselpack", "rpack", "sksel", "sr", "kmean", "kpart", "vmu",
                                                "total_bytes")] + \
                [(n, ctypes.c_int32) for n in ("n_ktiles", "n_qtiles", "s_pad_q", "n_sel_max", "n_sel_tiles_max")]
 

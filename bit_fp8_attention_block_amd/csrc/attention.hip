@@ -130,19 +130,17 @@ constexpr int NWAVES = 8;         // 2 waves per SIMD: one of each group
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int NBUF = 4;                    // K and V tiles, four buffers each
 constexpr int LDS_BYTES = 2 * NBUF * TILE_BYTES;
-// V-Smooth: the tile's scaled block means (128 fp32 = 512 B) ride with each V
-// tile in a 1 KiB slot
-constexpr int MU_SLOT = 1024;
-// eight slots: the mean term of four tiles is added at once (vsmooth_flush)
+// V-Smooth: the tile's block means (128 bf16 = 256 B) ride with each V tile
+constexpr int MU_SLOT = 256;
+// 32 slots: the mean term of sixteen tiles is added at once (vsmooth_flush)
 // while the means of later tiles are being loaded
-constexpr int MU_NBUF = 8;
+constexpr int MU_NBUF = 32;
 constexpr int LDS_BYTES_VS = LDS_BYTES + MU_NBUF * MU_SLOT;
 
-// The 512 bytes of one tile's scaled block means into a 1 KiB LDS slot by one
-// wave's direct load (voff = 16*(lane%32): lanes 32-63 repeat lanes 0-31 into
-// the upper half).
+// The 256 bytes of one tile's block means into an LDS slot by one wave's
+// direct load of 4 bytes per lane (voff = 4*lane)
 __device__ inline void load_means(uint32_t lds_dst, const uint8_t* src, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
                :
                : "s"(lds_dst), "v"(voff), "s"(src)
                : "memory", "m0");
@@ -245,47 +243,74 @@ __device__ __forceinline__ void pv_tile(const uint8_t* vt, v8i (&P)[QBW], const 
 }
 
 // V-Smooth restore. The output gains sum_t l_t * mu_t, with l_t the row sum of
-// tile t's weights and mu_t its block means (scaled by inv; the output is
-// multiplied by sv = 1/inv at the end). This is a contraction over tiles, so
-// it runs on the MFMA: four tiles at a time as one v_mfma_f32_16x16x4_f32
-// per 16 channels and 16 queries, O^T[d][q] += sum_k mu_k[d] * l_k[q].
+// tile t's weights and mu_t its bf16 block means (times inv = 448/amax of the
+// head's smoothed V; the output is multiplied by sv = 1/inv at the end). This
+// is a contraction over tiles, so it runs on the MFMA, sixteen tiles at a
+// time: O^T[d][q] += sum_k mu_k[d] * (inv * l_k[q]).
 //
-// vsmooth_tile: the row sum l = 1 * P^T (MFMA; every lane gets the sum of its
-// query), L += l, and l goes to the B operand lb of the batch: lanes of group
-// g = slot hold row k = slot (the tile's place in its batch of four).
-__device__ __forceinline__ void vsmooth_tile(const v8i (&P)[QBW], const int (&sb)[QBW], v4f (&L)[QBW], float (&lb)[QBW],
-                                             int slot, int g, const v8i& ones) {
+// vsmooth_tile: the row sum of tile t goes into row k = t%16 of the
+// accumulator C (C[k][q] += l_t[q]). The row-sum MFMA takes the all-ones A
+// operand with E8M0 scale 1 on the lanes of row k (asel = 127 where
+// l16 == k) and 2^-127 on the others (asel = 0), so the other rows gain at
+// most 2^-127 * l_t, far below the output's rounding.
+__device__ __forceinline__ void vsmooth_tile(const v8i (&P)[QBW], const int (&sb)[QBW], v4f (&C)[QBW], int asel,
+                                             const v8i& ones) {
 #pragma unroll
-  for (int qb = 0; qb < QBW; ++qb) {
-    const v4f l = mfma_f8_sb(ones, P[qb], v4f{0.f, 0.f, 0.f, 0.f}, sb[qb]);
-    L[qb] += l;
-    lb[qb] = g == slot ? l[0] : lb[qb];
-  }
+  for (int qb = 0; qb < QBW; ++qb)
+    C[qb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, P[qb], C[qb], 0, 0, 0, asel, 0, sb[qb]);
 }
 
-// vsmooth_flush: adds the batch whose last tile is step `last` (slots
-// 0..last%4). Lane (g, i) supplies A[i][g] = mu[16n + i] of the batch's tile g,
-// read from that tile's LDS slot, which holds the 128 scaled means in the
-// order [i][n] (channel 16n + i at 8i + n). Slots past `last` contribute
-// zero; lb is cleared for the next batch.
-__device__ __forceinline__ void vsmooth_flush(const uint8_t* mubuf, int last, v4f (&O)[QBW][8], float (&lb)[QBW],
-                                              int g, int l16) {
-  const int t = last - (last & 3) + g;
-  const bool valid = g <= (last & 3);
-  const v4f* m = reinterpret_cast<const v4f*>(mubuf + (t & (MU_NBUF - 1)) * MU_SLOT + 32 * l16);
-  const v4f m0 = m[0], m1 = m[1];
-  float av[8];
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+
+// vsmooth_flush: adds the batch of steps last - last%16 .. last and clears C.
+// C is in the layout of the bf16 16x16x16 MFMA's B operand (lane (q, g) holds
+// rows 4g..4g+3 of query q). inv * C is split into a truncated bf16 high part
+// and a bf16 low part (truncated too; error below 2^-16 of the value), and
+// each goes through one MFMA per 16 channels with the means as A: lane
+// (i, g) holds mu[16n + i] of the batch's steps 4g..4g+3, read as 2-byte
+// values from their LDS slots. Slots of steps past `last` hold older means
+// or zeros, against rows of C that hold no row sum. L gains the column sums
+// of C (over the 4 lanes of each query).
+__device__ __forceinline__ void vsmooth_flush(const uint8_t* mubuf, int last, float inv, v4f (&O)[QBW][8],
+                                              v4f (&L)[QBW], v4f (&C)[QBW], int g, int l16) {
+  const int s0 = last & ~15;
+  const uint16_t* mp[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    av[r] = valid ? m0[r] : 0.0f;
-    av[4 + r] = valid ? m1[r] : 0.0f;
+  for (int i = 0; i < 4; ++i)
+    mp[i] = reinterpret_cast<const uint16_t*>(mubuf + ((s0 + 4 * g + i) & (MU_NBUF - 1)) * MU_SLOT) + l16;
+  v4s A[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) A[n][i] = (short)mp[i][16 * n];
+  v4s Bh[QBW], Bl[QBW];
+#pragma unroll
+  for (int qb = 0; qb < QBW; ++qb) {
+    float cs = (C[qb][0] + C[qb][1]) + (C[qb][2] + C[qb][3]);
+    cs += __shfl_xor(cs, 16);
+    cs += __shfl_xor(cs, 32);
+    L[qb] += cs;
+    uint32_t u[4], w[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float c = C[qb][r] * inv;
+      u[r] = __float_as_uint(c);
+      w[r] = __float_as_uint(c - __uint_as_float(u[r] & 0xFFFF0000u));
+    }
+    const uint32_t h01 = __builtin_amdgcn_perm(u[1], u[0], 0x07060302u), h23 = __builtin_amdgcn_perm(u[3], u[2], 0x07060302u);
+    const uint32_t l01 = __builtin_amdgcn_perm(w[1], w[0], 0x07060302u), l23 = __builtin_amdgcn_perm(w[3], w[2], 0x07060302u);
+    Bh[qb] = __builtin_bit_cast(v4s, v2u{h01, h23});
+    Bl[qb] = __builtin_bit_cast(v4s, v2u{l01, l23});
+    C[qb] = v4f{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int n = 0; n < 8; ++n)
 #pragma unroll
-    for (int qb = 0; qb < QBW; ++qb) O[qb][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[n], lb[qb], O[qb][n], 0, 0, 0);
-#pragma unroll
-  for (int qb = 0; qb < QBW; ++qb) lb[qb] = 0.0f;
+    for (int qb = 0; qb < QBW; ++qb) {
+      O[qb][n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A[n], Bh[qb], O[qb][n], 0, 0, 0);
+      O[qb][n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A[n], Bl[qb], O[qb][n], 0, 0, 0);
+    }
 }
 
 // NaN-propagating maximum: scores are finite or -inf, and unlike fmaxf this
@@ -377,7 +402,7 @@ __device__ __forceinline__ void spread_pair(float v, float& v0, float& v1) {
 template <bool DUMP, bool EXPP>
 __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], float aq8, float skj, float& Mv,
                                              float& Mr, int (&sb)[QBW], v4f (&O)[QBW][8], v4f (&L)[QBW],
-                                             float (&lb)[QBW], int j, bool masked, const AttnArgs& a, int g,
+                                             v4f (&C)[QBW], int j, bool masked, const AttnArgs& a, int g,
                                              int qrow0) {
   if (masked) {
     // keys beyond S in the last (ragged) tile take no part in max or sums.
@@ -421,7 +446,8 @@ __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], fl
           for (int r = 0; r < 4; ++r) O[qb][n][r] = __builtin_ldexpf(O[qb][n][r], d[qb]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) L[qb][r] = __builtin_ldexpf(L[qb][r], d[qb]);
-        lb[qb] = __builtin_ldexpf(lb[qb], d[qb]);   // V-Smooth row sums not yet added
+#pragma unroll
+        for (int r = 0; r < 4; ++r) C[qb][r] = __builtin_ldexpf(C[qb][r], d[qb]);   // V-Smooth row sums not yet added
       }
       Mr = re ? Mn : Mr;
       e = re ? 0.0f : e;
@@ -537,7 +563,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   // LDS offsets of the K, V and block-mean buffers, and the per-lane offsets
   // of the direct loads
   const uint32_t kofs = lds_offset(kbuf), vofs = lds_offset(vbuf), mofs = lds_offset(mubuf);
-  const uint32_t voff = 16u * tid, voff_mu = 16u * (lane & 31);
+  const uint32_t voff = 16u * tid, voff_mu = 4u * lane;
   const int q0 = qt * BQ + wv * QBW * 16;
   const int qrow0 = q0 + l16;
   const int nT = a.nT;
@@ -563,7 +589,8 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   asm volatile("" : "+v"(ones));
   v4f O[QBW][8], L[QBW], S[QBW][8];
   v8i P[QBW];
-  float Mv = -16384.0f, lb[QBW];   // running max per block by row parity (see expcast_tile)
+  float Mv = -16384.0f;            // running max per block by row parity (see expcast_tile)
+  v4f C[QBW];                      // V-Smooth: row sums of the current batch of sixteen tiles
   float Mr = -16384.0f;            // reference max of O and L, same layout
   int sb[QBW] = {127, 127};        // E8M0 scale of the P operand: 2^(M - Mr)
   int one = 127;                   // the V operand's unit scale, in a register
@@ -572,7 +599,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int qb = 0; qb < QBW; ++qb) {
     L[qb] = v4f{0.f, 0.f, 0.f, 0.f};
-    lb[qb] = 0.0f;
+    C[qb] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int n = 0; n < 8; ++n) O[qb][n] = v4f{0.f, 0.f, 0.f, 0.f};
   }
@@ -596,8 +623,16 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   for (int i = 0; i < 2; ++i)
     if (i < nT) load_tile<NTHREADS>(vofs + i * TILE_BYTES, vt_ptr(i), voff, wvs);
   const auto mu_ptr = [&](int step) {
-    return reinterpret_cast<const uint8_t*>(a.vmus + ((int64_t)bh * nT + tile_at(step, centre, nT, a.order)) * HEAD_DIM);
+    return reinterpret_cast<const uint8_t*>(a.vmu + ((int64_t)bh * nT + tile_at(step, centre, nT, a.order)) * HEAD_DIM);
   };
+  const float vinv = VSMOOTH ? a.sv[2 * bh + 1] : 0.0f;
+  if (VSMOOTH) {
+    // slots of steps never loaded are read by the last flush of a short
+    // sequence (against rows of C without a row sum): zero, not stale LDS
+    static_assert(MU_NBUF * MU_SLOT == 16 * NTHREADS, "one 16-byte store per thread");
+    *reinterpret_cast<uint4*>(mubuf + 16 * tid) = uint4{0u, 0u, 0u, 0u};
+    __syncthreads();
+  }
   if (VSMOOTH && wv == 0) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -635,20 +670,28 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
     if (ld_mu) load_means(mofs + ((s + 2) & (MU_NBUF - 1)) * MU_SLOT, mu_ptr(s + 2), voff_mu);
     const float skj = skp[j];
     if (!GB) {
-      expcast_tile<DUMP, EXPP>(S, P, aq8, skj, Mv, Mr, sb, O, L, lb, j, j == last_masked, a, g, qrow0);
-      if (VSMOOTH) vsmooth_tile(P, sb, L, lb, s & 3, g, ones);
+      expcast_tile<DUMP, EXPP>(S, P, aq8, skj, Mv, Mr, sb, O, L, C, j, j == last_masked, a, g, qrow0);
+      if (VSMOOTH) vsmooth_tile(P, sb, C, l16 == (s & 15) ? 127 : 0, ones);
       pv_tile<!VSMOOTH, true>(vbuf + b0 * TILE_BYTES, P, sb, one, O, L, lane, ones, pre);
-      if (VSMOOTH && ((s & 3) == 3 || s + 1 == nT)) { ofence(O); vsmooth_flush(mubuf, s, O, lb, g, l16); }
+      if (VSMOOTH && ((s & 15) == 15 || s + 1 == nT)) {
+        ofence(O);
+        vsmooth_flush(mubuf, s, vinv, O, L, C, g, l16);
+        ofence(O);
+      }
       if (s + 1 < nT) qk_tile(kbuf + b1 * TILE_BYTES, qop, S, lane);
     } else {
       __builtin_amdgcn_s_setprio(2);
       qk_tile<KPRE>(kbuf + b0 * TILE_BYTES, qop, S, lane, pre);
       if (s > 0) pv_tile<!VSMOOTH, true>(vbuf + bm1 * TILE_BYTES, P, sb, one, O, L, lane, ones, bpre);
       // the batch that ended with tile s-1 (before ExpCast(s) may re-anchor)
-      if (VSMOOTH && s > 0 && ((s - 1) & 3) == 3) { ofence(O); vsmooth_flush(mubuf, s - 1, O, lb, g, l16); }
+      if (VSMOOTH && s > 0 && ((s - 1) & 15) == 15) {
+        ofence(O);
+        vsmooth_flush(mubuf, s - 1, vinv, O, L, C, g, l16);
+        ofence(O);
+      }
       __builtin_amdgcn_s_setprio(0);
-      expcast_tile<DUMP, EXPP>(S, P, aq8, skj, Mv, Mr, sb, O, L, lb, j, j == last_masked, a, g, qrow0);
-      if (VSMOOTH) vsmooth_tile(P, sb, L, lb, s & 3, g, ones);
+      expcast_tile<DUMP, EXPP>(S, P, aq8, skj, Mv, Mr, sb, O, L, C, j, j == last_masked, a, g, qrow0);
+      if (VSMOOTH) vsmooth_tile(P, sb, C, l16 == (s & 15) ? 127 : 0, ones);
       // K step s+1 and V step s have been in LDS since the last barrier: the
       // first operands of the next QK and PV arrive before the next one
       if (s + 1 < nT) {
@@ -681,7 +724,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
     pv_tile<!VSMOOTH, true>(vbuf + ((nT - 1) & (NBUF - 1)) * TILE_BYTES, P, sb, one, O, L, lane, ones, bpre);
     if (VSMOOTH) {
       ofence(O);
-      vsmooth_flush(mubuf, nT - 1, O, lb, g, l16);
+      vsmooth_flush(mubuf, nT - 1, vinv, O, L, C, g, l16);
     }
   }
   {
@@ -806,7 +849,7 @@ static hipError_t launch_variant(const AttnArgs& a, bool repair, bool dump, dim3
 hipError_t launch_attention(const AttnArgs& a, bool repair, bool dump, hipStream_t st) {
   const int nwork = a.B * a.H * a.nQT;
   const dim3 grid = dump ? dim3(a.nQT) : dim3(8 * ((nwork + 7) / 8));
-  if (a.vmus != nullptr)
+  if (a.vmu != nullptr)
     return a.exp_path ? launch_variant<true, true>(a, repair, dump, grid, st)
                       : launch_variant<false, true>(a, repair, dump, grid, st);
   return a.exp_path ? launch_variant<true, false>(a, repair, dump, grid, st)

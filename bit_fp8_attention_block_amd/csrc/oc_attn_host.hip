@@ -127,7 +127,6 @@ static void compute_layout(oc_attn_plan* p) {
   L.kmean = take(BH * HEAD_DIM * 4);
   L.kpart = take(BH * L.n_ktiles * (uint64_t)HEAD_DIM * 8);
   L.vmu = take(BH * L.n_ktiles * (uint64_t)HEAD_DIM * 2);
-  L.vmus = take(BH * L.n_ktiles * (uint64_t)HEAD_DIM * 4);
   L.total_bytes = off;
 }
 
@@ -202,7 +201,6 @@ static PrepArgs prep_args(const oc_attn_plan* p, const void* q, const void* k, c
   }
   if (p->v_smooth) {
     a.vmu = (uint16_t*)(base + L.vmu);
-    a.vmus = (float*)(base + L.vmus);
   }
   if (n_sel > 0) {
     a.energy = (double*)(base + L.energy);
@@ -248,7 +246,7 @@ static AttnArgs attn_args(const oc_attn_plan* p, const void* ws, void* out, int 
   a.c8 = (float)(8.0 * (double)p->tau * 1.4426950408889634);
   a.order = p->order;
   a.exp_path = p->exp_path;
-  a.vmus = p->prepared_vsmooth(ws) ? (const float*)(base + L.vmus) : nullptr;
+  a.vmu = p->prepared_vsmooth(ws) ? (const uint16_t*)(base + L.vmu) : nullptr;
   return a;
 }
 

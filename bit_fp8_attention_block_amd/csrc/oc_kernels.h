@@ -26,7 +26,6 @@ struct PrepArgs {
   double* kpart;               // [B][H][nT][128] per-block key sums
   // V-Smooth block means (vmu == nullptr: off)
   uint16_t* vmu;               // [B][H][nT][128] bf16 block means
-  float* vmus;                 // [B][H][nT][128] mean * (448/amax), channel 16n+i at 8i+n
   // repair (energy == nullptr: no repair)
   double* energy;
   int32_t* sel;
@@ -54,7 +53,7 @@ struct AttnArgs {
   float c8;                    // 8 * tau * log2(e)
   int order;                   // 0: from the middle of the key window outwards, 1: ascending
   int exp_path;                // 0: ExpCast bytes; 1: exp2 + FP32->E4M3 cast (comparison path)
-  const float* vmus;           // V-Smooth: [B][H][nT][128] scaled block means (nullptr: off)
+  const uint16_t* vmu;         // V-Smooth: [B][H][nT][128] bf16 block means (nullptr: off)
   uint8_t* dump_codes;         // debug: [S][S] bytes for one (b, h)
   int32_t* dump_m;             // debug: [S][nT]
   int dump_b, dump_h;

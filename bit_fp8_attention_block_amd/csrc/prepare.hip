@@ -300,12 +300,6 @@ __global__ __launch_bounds__(256) void prep_v_kernel(PrepArgs a) {
 #pragma unroll
   for (int c = 0; c < 16; ++c)
     mu[c] = VSMOOTH ? bf16_to_f32(a.vmu[((int64_t)bh * a.nT + tile) * HEAD_DIM + 16 * oc + c]) : 0.0f;
-  if (VSMOOTH && m == 0) {
-    // mu * inv for channel d = 16n + i at 8i + n (n = oc, i = c here): the
-    // attention kernel's lane i reads its 8 channels as one 32-byte row
-#pragma unroll
-    for (int c = 0; c < 16; ++c) a.vmus[((int64_t)bh * a.nT + tile) * HEAD_DIM + 8 * c + oc] = mu[c] * inv;
-  }
   uint4 lo[4], hi[4], cd[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {

@@ -124,15 +124,11 @@ typedef struct oc_attn_desc {
  *   vmu    bf16 [B][H][n_ktiles][128] V block means (V-Smooth only; vpack then
  *                                     holds the codes of v - mean, and sv and
  *                                     vamax refer to those residuals)
- *   vmus   f32 [B][H][n_ktiles][128]  mean * 448/amax in the order of the
- *                                     attention kernel's mean-term operand:
- *                                     slot 8i + n holds channel 16n + i
- *                                     (V-Smooth only)
  */
 typedef struct oc_attn_ws_layout {
   uint64_t qhat, kpack, vpack, sq, sk, vamax, sv;
   uint64_t energy, sel, kselpack, rpack, sksel, sr;
-  uint64_t kmean, kpart, vmu, vmus;
+  uint64_t kmean, kpart, vmu;
   uint64_t total_bytes;
   int32_t n_ktiles, n_qtiles, s_pad_q, n_sel_max, n_sel_tiles_max;
 } oc_attn_ws_layout;

@@ -122,10 +122,6 @@ class WsView:
         n = self.L.n_ktiles * 128
         return self._arr(self.L.vmu + 2 * n * self.bh(b, h), np.uint16, n).reshape(self.L.n_ktiles, 128)
 
-    def vmus(self, b, h):
-        n = self.L.n_ktiles * 128
-        return self._arr(self.L.vmus + 4 * n * self.bh(b, h), np.float32, n).reshape(self.L.n_ktiles, 128)
-
     def kmean(self, b, h):
         return self._arr(self.L.kmean + 4 * 128 * self.bh(b, h), np.float32, 128)
 

@@ -210,6 +210,6 @@ def test_set_v_smoothing_accepts_0_and_1():
         L = oc.WsLayout()
         assert lib.oc_attn_workspace_layout(p, ctypes.byref(L)) == oc.OC_OK
         nT = math.ceil(1000 / 128)
-        assert L.vmus >= L.vmu + 4 * nT * 128 * 2 and L.total_bytes >= L.vmus + 4 * nT * 128 * 4
+        assert L.total_bytes >= L.vmu + 4 * nT * 128 * 2
     finally:
         lib.oc_attn_plan_destroy(p)

@@ -210,7 +210,7 @@ def test_identical_keys_give_mean_value():
     assert oracle.rel_l2(got, np.tile(mean, (S, 1))) < 4e-3
 
 
-@pytest.mark.parametrize("variant", ["expcast", "exp_fp8", "repair"])
+@pytest.mark.parametrize("variant", ["expcast", "exp_fp8", "repair", "vsmooth"])
 def test_running_max_rising_by_many_binades(variant):
     """The kernel keeps O and L in the frame of a reference max and re-anchors
     them (by an exact power of two) once the running max has risen more than
@@ -220,9 +220,11 @@ def test_running_max_rising_by_many_binades(variant):
     their frame is re-anchored with O and L already non-zero, while the other
     16 queries of the same waves behave normally. (The large logit is spread
     over 64 equal products: a single dominant product would instead test the
-    FP8 MFMA's summation precision, which is coarser than fp32.)"""
+    FP8 MFMA's summation precision, which is coarser than fp32.) With V-Smooth
+    the row sums waiting for the next mean-term batch are re-anchored too; its
+    20 tiles put a batch boundary among the re-anchors."""
     oc = _oc()
-    S = 1024
+    S = 2560 if variant == "vsmooth" else 1024
     g = torch.Generator().manual_seed(31)
     q = torch.randn(1, S, 1, 128, generator=g) * 0.5
     k = torch.randn(1, S, 1, 128, generator=g) * 0.5
@@ -237,6 +239,10 @@ def test_running_max_rising_by_many_binades(variant):
         prep = oc.prepare_v_repair(q, k, v, 0.02)
         out = oc.attention_v_repair(q, k, v, 0.02)
         opts = dict(budget=0.02)
+    elif variant == "vsmooth":
+        prep = oc.prepare(q, k, v, v_smooth=True)
+        out = oc.attention(q, k, v, v_smooth=True)
+        opts = dict(v_smooth=True)
     else:
         prep = oc.prepare(q, k, v)
         out = oc.attention(q, k, v, weights=variant)

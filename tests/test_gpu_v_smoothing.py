@@ -29,15 +29,6 @@ def _biased_values(B, S, H, seed, dtype=torch.bfloat16):
     return tuple(t.to(dtype).cuda() for t in (q, k, v))
 
 
-def _lane_order(mu_scaled):
-    """[n, 128] per channel -> slot 8i + n holds channel 16n + i"""
-    out = np.empty_like(mu_scaled)
-    for d in range(128):
-        n, i = d >> 4, d & 15
-        out[:, 8 * i + n] = mu_scaled[:, d]
-    return out
-
-
 @pytest.mark.parametrize("case", ["s1024_h2", "ragged_fp16", "biased", "repair"])
 def test_smoothed_value_prepare_bit_exact(case):
     oc = _oc()
@@ -63,10 +54,8 @@ def test_smoothed_value_prepare_bit_exact(case):
             mu_bits = (ph.vmean.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
             assert np.array_equal(w.vmu(b, h), mu_bits), (b, h, "block means")
             assert np.array_equal(w.vcodes(b, h), ph.vc), (b, h, "residual codes")
-            s, inv = w.sv(b, h)
+            s, _ = w.sv(b, h)
             assert s == ph.sv, (b, h, "residual scale")
-            want = _lane_order(ph.vmean.astype(np.float32) * np.float32(inv))
-            assert np.array_equal(w.vmus(b, h), want), (b, h, "scaled means")
             if budget:
                 rp = ph.repair
                 assert np.array_equal(w.energy(b, h), rp.energy) or np.allclose(w.energy(b, h), rp.energy,
@@ -92,11 +81,12 @@ def test_smoothed_value_attention_matches_oracle(name):
     _compare(q, k, v, out, pairs, rows, label=name + " V-Smooth", prep=prep, v_smooth=True)
 
 
-@pytest.mark.parametrize("S", [1, 5, 130, 300, 700, 1000, 1500])
+@pytest.mark.parametrize("S", [1, 5, 130, 300, 700, 1000, 1500, 2100, 4200])
 def test_smoothed_value_attention_ragged_batches(S):
-    """The mean term is added four key tiles at a time; these lengths give
-    1, 1, 2, 3, 6, 8 and 12 tiles, so the last batch is partial or full in
-    both wave groups, and the last tile is ragged."""
+    """The mean term is added sixteen key tiles at a time; these lengths give
+    1, 1, 2, 3, 6, 8, 12, 17 and 33 tiles, so the last batch is partial (down
+    to one tile after full ones) in both wave groups, and the last tile is
+    ragged."""
     oc = _oc()
     log(f"[v-smooth ragged] S={S}")
     q, k, v = _biased_values(1, S, 2, seed=11 + S)
@@ -107,7 +97,7 @@ def test_smoothed_value_attention_ragged_batches(S):
 
 
 def test_smoothed_value_attention_full_size_sampled():
-    """S=73397, H=56 (574 key tiles: the last batch holds two), sampled rows of
+    """S=73397, H=56 (574 key tiles: the last batch holds fourteen), sampled rows of
     three heads, including the ragged tail."""
     oc = _oc()
     name = "s73397_h56"
