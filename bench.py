@@ -40,7 +40,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 # rocprofv3 PMC counters (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors a
 # plain 4 GiB copy gives; profiles/attn_kernel_s73397_h56.md). They are only
 # reported while the kernel sources still hash to the measured version.
-MEASURED_TRAFFIC = {"sources_sha256": "c8c0bf82f8925e1da78c98b5e3823c87cb540f103b627a58f292fece5ac35203", "bytes": 11962765504}
+MEASURED_TRAFFIC = {"sources_sha256": "65406fbd42fbb56fa640e9c28f8a002fd361e21b8e7baad8e25b2c602685fdd0", "bytes": 11962702795}
 KERNEL_SOURCES = ("bit_fp8_attention_block_amd/csrc/attention.hip", "bit_fp8_attention_block_amd/csrc/oc_common.h")
 
 

@@ -271,7 +271,10 @@ typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 // (i, g) holds mu[16n + i] of the batch's steps 4g..4g+3, read as 2-byte
 // values from their LDS slots. Slots of steps past `last` hold older means
 // or zeros, against rows of C that hold no row sum. L gains the column sums
-// of C (over the 4 lanes of each query).
+// of C (over the 4 lanes of each query). C reaches 2^83 in the frame (16
+// tiles x 128 keys x 256 x 2^64), so where inv exceeds 2^40 (amax of the
+// smoothed V below about 4e-10) the excess power of two goes onto the means
+// instead, exactly (through fp32); inv * C stays below 2^124.
 __device__ __forceinline__ void vsmooth_flush(const uint8_t* mubuf, int last, float inv, v4f (&O)[QBW][8],
                                               v4f (&L)[QBW], v4f (&C)[QBW], int g, int l16) {
   const int s0 = last & ~15;
@@ -279,11 +282,23 @@ __device__ __forceinline__ void vsmooth_flush(const uint8_t* mubuf, int last, fl
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     mp[i] = reinterpret_cast<const uint16_t*>(mubuf + ((s0 + 4 * g + i) & (MU_NBUF - 1)) * MU_SLOT) + l16;
+  int ash = 0;   // uniform: inv is the head's
+  if (inv > 0x1p40f) {
+    ash = (int)(__float_as_uint(inv) >> 23) - 127 - 40;   // inv is positive and normal here
+    inv = __builtin_ldexpf(inv, -ash);
+  }
   v4s A[8];
 #pragma unroll
   for (int n = 0; n < 8; ++n)
 #pragma unroll
     for (int i = 0; i < 4; ++i) A[n][i] = (short)mp[i][16 * n];
+  if (ash > 0) {
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        A[n][i] = (short)(__float_as_uint(__builtin_ldexpf(__uint_as_float((uint32_t)(uint16_t)A[n][i] << 16), ash)) >> 16);
+  }
   v4s Bh[QBW], Bl[QBW];
 #pragma unroll
   for (int qb = 0; qb < QBW; ++qb) {

@@ -174,9 +174,6 @@ oc_status oc_attn_plan_set_k_smoothing(oc_attn_plan* plan, int enable);
  * selection) acts on fp32(v - mu). The attention on such a workspace adds the
  * means back with each key tile's row sum:
  *   O_i = (sv * sum_j P_ij dec(r_j) + sum_t l_it mu_t) / L_i.
- * Range: a head whose smoothed values have amax below about 1.3e-11 may give
- * non-finite outputs (the kernel's intermediate row sums times 448/amax can
- * exceed fp32); there is no error code for it.
  * oc_attn_forward_prepared follows the setting the workspace was prepared
  * with. enable must be 0 or 1, else OC_ERR_INVALID_ARGUMENT. */
 oc_status oc_attn_plan_set_v_smoothing(oc_attn_plan* plan, int enable);
