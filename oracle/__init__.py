@@ -17,6 +17,6 @@ from .expcast import (  # noqa: F401
     BETA, CODE_OF_PMAX, QK_BLOCK, PreparedHead, RepairSet, bitaligned_row_max,
     exact_attention_head, exp_cast_codes, expcast_attention_head, expcast_attention_online, expcast_codes,
     key_mean, key_tile_order, smooth_keys, smooth_values, to_bf16, value_block_means,
-    log2_logits, prepare_head, quant_scale, quantize_blocks, quantize_head,
+    log2_logits, prepare_head, quant_scale, quantize_blocks, quantize_head, residual_energy, SCALE_FLOOR,
     quantize_with, rel_l2, repair_count, repair_select, row_total_variation,
 )

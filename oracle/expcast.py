@@ -33,8 +33,9 @@ Readings where the pages leave a step open:
     outwards, bytes relative to the running M, exact power-of-two rescales.
   * the row sum is over the decoded weights: L = sum_j dec(c_j).
   * Q/K scale blocks are 128 tokens x 128 channels; scale s = amax/448 in fp32,
-    quantization multiplies by the fp32 reciprocal 448/amax; an all-zero
-    block gets s = 1.
+    quantization multiplies by the fp32 reciprocal 448/amax; a block whose
+    amax is below 2^-100 (an all-zero block included) gets s = 1 and so
+    codes 0.
   * K-mean smoothing (an option, off by default; the VC-Attention write-up,
     section on why attention is the bottleneck, names Q/K smoothing as prior
     practice): before the K blocks are quantized, every key loses the mean key
@@ -50,7 +51,8 @@ Readings where the pages leave a step open:
     sum_t l_it mu_t) / L_i, l_it = sum over tile t of P_ij. With repair, the
     repaired residual is taken of fp32(v - mu_t) in place of v.
   * repair: residual r = v - sv*dec(v_hat) in fp32; energy = sum over the 128
-    channels of r^2 accumulated in float64 in channel order; the top
+    channels of r^2 in float64, added pairwise up a balanced binary tree in
+    channel order (residual_energy); the top
     k = ceil(budget*S) tokens by energy (ties to the lower index) are repaired
     with an E4M3 residual carrying its own per-head scale; the row sums L are
     left unchanged. The budget is a float64 fraction of the tokens.
@@ -71,11 +73,19 @@ LOG2E = 1.0 / math.log(2.0)
 F32 = np.float32
 
 
+# A block (or head, or repair set) whose amax lies below this is quantized with
+# the unit scale, like an all-zero block: 448/amax would otherwise approach
+# the top of the fp32 range (and overflow below about 1.3e-36), while every
+# element rounds to code 0 under the unit scale anyway.
+SCALE_FLOOR = 2.0 ** -100
+
+
 def quant_scale(amax: float):
     """fp32 dequantization scale s = amax/448 and quantization multiplier
-    inv = 448/amax, both correctly rounded fp32 divisions. amax == 0 -> (1, 1)."""
+    inv = 448/amax, both correctly rounded fp32 divisions. amax below
+    2^-100 (zero included) -> (1, 1)."""
     a = F32(amax)
-    if a == 0:
+    if a < F32(SCALE_FLOOR):
         return F32(1.0), F32(1.0)
     return F32(a / F32(448.0)), F32(F32(448.0) / a)
 
@@ -141,6 +151,20 @@ def repair_count(budget: float, S: int) -> int:
     return max(0, min(S, int(math.ceil(b * S - 1e-9))))
 
 
+def residual_energy(r: np.ndarray) -> np.ndarray:
+    """Per token, the sum over the 128 channels of r^2 in float64, added by
+    pairwise summation in channel order: neighbouring channels first, then
+    neighbouring pairs, and so on up a balanced binary tree (seven levels).
+    Each square of an fp32 residual is exact in float64, so only the order of
+    the additions decides the rounding, and this order fixes it."""
+    e = r.astype(np.float64) ** 2
+    if e.shape[1] & (e.shape[1] - 1):
+        raise ValueError("the channel count must be a power of two")
+    while e.shape[1] > 1:
+        e = e[:, 0::2] + e[:, 1::2]
+    return e[:, 0]
+
+
 def repair_select(v: np.ndarray, vc: np.ndarray, sv, budget: float) -> RepairSet:
     """Rank value tokens by the energy of their quantization residual and
     quantize the residual of the top-k tokens."""
@@ -148,7 +172,7 @@ def repair_select(v: np.ndarray, vc: np.ndarray, sv, budget: float) -> RepairSet
     k = repair_count(budget, S)
     t = F32(sv) * decode(vc).astype(F32)       # fp32 product sv*dec(v_hat)
     r = v.astype(F32) - t                      # fp32 residual
-    energy = np.cumsum(r.astype(np.float64) ** 2, axis=1)[:, -1]   # channel order
+    energy = residual_energy(r)
     order = np.lexsort((np.arange(S), -energy))  # energy descending, then index ascending
     sel = np.sort(order[:k])
     if k == 0:

@@ -35,7 +35,7 @@ def _enc(y):
 
 
 def _scales(amax):
-    if amax == 0:
+    if amax < 2.0 ** -100:            # all-zero and tiny blocks: unit scale, every code 0
         return np.float32(1), np.float32(1)
     a = np.float32(amax)
     return np.float32(a / np.float32(448)), np.float32(np.float32(448) / a)
@@ -199,11 +199,23 @@ def test_error_vs_exact_on_small_workload():
 
 # ---- the single-pass (online) form --------------------------------------
 
-def brute_force_online(q, k, v, order, tau=TAU, weights="expcast"):
+def _pairwise(xs):
+    """pairwise summation by recursive halving"""
+    if len(xs) == 1:
+        return xs[0]
+    h = len(xs) // 2
+    return _pairwise(xs[:h]) + _pairwise(xs[h:])
+
+
+def brute_force_online(q, k, v, order, tau=TAU, weights="expcast", budget=0.0):
     """Online ExpCast attention with explicit loops: key tiles of 128 in the
     given order, running integer max raised before each tile's bytes, running
     sums multiplied by 2**(M_old - M_new). weights="exp_cast" takes each byte
-    as the E4M3 cast of the fp32 weight 2**(x - M + 8) instead."""
+    as the E4M3 cast of the fp32 weight 2**(x - M + 8) instead. With a budget,
+    the ceil(budget*S) tokens whose fp32 residual v - sv*dec(v_hat) has the
+    largest energy (sum of squares, pairwise; ties to the lower index) get
+    their E4M3-quantized residual added to the value after the last tile,
+    weighted by bytes against the final max, with the row sum unchanged."""
     S, D = len(k), len(k[0])
     qc, kc, sq, sk = [None] * S, [None] * S, [0.0] * S, [0.0] * S
     for x, codes, sc in ((q, qc, sq), (k, kc, sk)):
@@ -215,6 +227,15 @@ def brute_force_online(q, k, v, order, tau=TAU, weights="expcast"):
                 sc[i] = float(s)
     sv, invv = _scales(max(abs(v[i][c]) for i in range(S) for c in range(D)))
     vd = [[_dec(_enc(float(np.float32(v[i][c]) * invv))) for c in range(D)] for i in range(S)]
+    sel, rd, sr = [], [], 0.0
+    kk = math.ceil(budget * S - 1e-9) if budget > 0 else 0
+    if kk:
+        res = [[np.float32(np.float32(v[j][c]) - np.float32(sv) * np.float32(vd[j][c])) for c in range(D)]
+               for j in range(S)]
+        energy = [_pairwise([float(x) * float(x) for x in res[j]]) for j in range(S)]
+        sel = sorted(sorted(range(S), key=lambda j: (-energy[j], j))[:kk])
+        sr, invr = _scales(max(abs(float(res[j][c])) for j in sel for c in range(D)))
+        rd = [[_dec(_enc(float(np.float32(res[j][c]) * invr))) for c in range(D)] for j in sel]
     out = []
     for i in range(S):
         M, L, O = None, 0.0, [0.0] * D
@@ -237,7 +258,17 @@ def brute_force_online(q, k, v, order, tau=TAU, weights="expcast"):
                 L += w
                 for c in range(D):
                     O[c] += w * vd[j][c]
-        out.append([float(sv) * o / L for o in O])
+        O = [float(sv) * o for o in O]
+        for n, j in enumerate(sel):
+            dot = sum(_dec(qc[i][c]) * _dec(kc[j][c]) for c in range(D))
+            xj = tau * LOG2E * dot * (sq[i] * sk[j])
+            if weights == "expcast":
+                w = _dec(min(126, max(0, round(8 * (xj - M) + 120 - 0.35))))
+            else:
+                w = _dec(_enc(float(np.float32(2.0 ** (xj - M + 8)))))
+            for c in range(D):
+                O[c] += float(sr) * w * rd[n][c]
+        out.append([o / L for o in O])
     return np.array(out)
 
 
@@ -250,8 +281,8 @@ def test_key_tile_order_is_mid_window():
         assert sorted(oracle.key_tile_order(n)) == list(range(n))
 
 
-@pytest.mark.parametrize("S", [130, 300])
-def test_online_brute_force_matches_vectorized(S):
+@pytest.mark.parametrize("S,budget", [(130, 0.0), (300, 0.0), (130, 0.05), (300, 0.3)])
+def test_online_brute_force_matches_vectorized(S, budget):
     q, k, v = (t[0, :, 0].double().numpy() for t in workloads.random_qkv(1, S, 1, seed=S + 1, scale=2.0))
     # a strong key late in the order so the running max has to grow
     k[S - 1] = q[3] * 1.5
@@ -259,9 +290,13 @@ def test_online_brute_force_matches_vectorized(S):
     rows = [0, 3, 77, S - 1]
     nT = -(-S // 128)
     for order, name in ((oracle.key_tile_order(nT), "mid"), (list(range(nT)), "ascending")):
-        want = brute_force_online(q.tolist(), k.tolist(), v.tolist(), order)[rows]
-        got = oracle.expcast_attention_online(q, k, v, rows=rows, order=name)["out"]
+        want = brute_force_online(q.tolist(), k.tolist(), v.tolist(), order, budget=budget)[rows]
+        got = oracle.expcast_attention_online(q, k, v, rows=rows, order=name, budget=budget)["out"]
         np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+    if budget:
+        # the repair term is resolved: it moves the output far above the tolerance used here
+        plain = oracle.expcast_attention_online(q, k, v, rows=rows)["out"]
+        assert np.abs(plain - got).max() > 1e-4
 
 
 @pytest.mark.parametrize("S", [2, 17, 130])
@@ -406,9 +441,12 @@ def test_exp_cast_path_tracks_exact_weights_closer_than_expcast():
     assert tv(oracle.exp_cast_codes(x, M)).mean() < tv(oracle.expcast_codes(x, M)).mean()
 
 
-def test_online_equals_two_pass_when_max_is_visited_first():
+@pytest.mark.parametrize("budget", [0.0, 0.02, 0.3, 1.0])
+def test_online_equals_two_pass_when_max_is_visited_first(budget):
     """If every row's largest logit lies in the first tile visited, all bytes
-    are written against the final max and both forms coincide."""
+    are written against the final max and both forms coincide, the repair
+    term of the single-pass form (bytes of the selected keys against the
+    final max, unrepaired row sums) included."""
     S = 700
     rng = np.random.default_rng(4)
     q = rng.normal(0, 1, (S, 128))
@@ -419,8 +457,8 @@ def test_online_equals_two_pass_when_max_is_visited_first():
     v = rng.normal(0, 1, (S, 128))
     q, k, v = (torch.from_numpy(t).bfloat16().double().numpy() for t in (q, k, v))
     rows = np.arange(0, S, 5)
-    a = oracle.expcast_attention_online(q, k, v, rows=rows)
-    b = oracle.expcast_attention_head(q, k, v, rows=rows)
+    a = oracle.expcast_attention_online(q, k, v, rows=rows, budget=budget)
+    b = oracle.expcast_attention_head(q, k, v, rows=rows, budget=budget)
     np.testing.assert_array_equal(a["M"], b["M"])
     np.testing.assert_allclose(a["L"], b["L"], rtol=1e-13)
     np.testing.assert_allclose(a["out"], b["out"], rtol=1e-12, atol=1e-14)

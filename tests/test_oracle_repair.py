@@ -38,9 +38,17 @@ def test_budget_zero_equals_no_repair():
     assert np.array_equal(a, b)
 
 
+def _pairwise(xs):
+    """pairwise summation by recursive halving"""
+    if len(xs) == 1:
+        return xs[0]
+    h = len(xs) // 2
+    return _pairwise(xs[:h]) + _pairwise(xs[h:])
+
+
 def test_selection_matches_brute_force():
     """Energies recomputed token by token with Python floats (fp32 residual via
-    numpy scalars, float64 squares summed channel by channel), then a plain
+    numpy scalars, float64 squares added by recursive halving), then a plain
     sort: the selected set must match exactly."""
     q, k, v = _head(S=600)
     vc, sv = oracle.quantize_head(v)
@@ -48,11 +56,11 @@ def test_selection_matches_brute_force():
     dec = oracle.decode(vc)
     energies = []
     for j in range(len(v)):
-        e = 0.0
+        sq = []
         for c in range(128):
             r = np.float32(np.float32(v[j, c]) - np.float32(sv) * np.float32(dec[j, c]))
-            e += float(r) * float(r)
-        energies.append(e)
+            sq.append(float(r) * float(r))
+        energies.append(_pairwise(sq))
     assert np.array_equal(rp.energy, np.array(energies))
     kk = math.ceil(0.05 * 600)
     order = sorted(range(len(v)), key=lambda j: (-energies[j], j))
