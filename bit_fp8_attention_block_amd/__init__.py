@@ -20,6 +20,7 @@ contiguous channel dimension and 16-byte aligned rows. The output is bf16
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 
 import torch
@@ -77,7 +78,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.oc_attn_prepare_v_repair.argtypes = [P, VP, VP, VP, D, VP, SZ, VP]
     lib.oc_attn_forward_v_repair.argtypes = [P, VP, VP, VP, D, VP, VP, SZ, VP]
     lib.oc_attn_forward_prepared.argtypes = [P, VP, SZ, VP, ctypes.c_int, VP]
-    lib.oc_attn_debug_pcodes.argtypes = [P, VP, SZ, I32, I32, VP, VP, VP, VP]
+    lib.oc_attn_debug_pcodes.argtypes = [P, VP, SZ, I32, I32, VP, I32, I32, VP, VP, VP, VP, VP, VP, VP]
     lib.oc_attn_status_string.argtypes = [st]
     lib.oc_attn_status_string.restype = ctypes.c_char_p
     lib.oc_attn_last_hip_error.argtypes = []
@@ -176,6 +177,14 @@ class Prepared:
         self.plan, self.ws, self.shape, self.device = plan, ws, shape, device
         self.budget, self.softmax_scale = budget, softmax_scale
 
+    @property
+    def n_sel(self):
+        """selected tokens per (b, h): ceil(budget*S), as the library counts them"""
+        if not self.budget:
+            return 0
+        S = self.shape[1]
+        return max(0, min(S, math.ceil(self.budget * S - 1e-9)))
+
     def tensor(self, name, dtype, count):
         off = getattr(self.plan.layout, name)
         nbytes = count * torch.empty(0, dtype=dtype).element_size()
@@ -198,12 +207,17 @@ def get_plan(q, softmax_scale=None, max_budget=0.0):
 
 
 def _workspace(plan, device):
-    ws = getattr(plan, "_ws", None)
-    if ws is None or ws.device != device:
+    """The plan's workspace for the current stream of `device`: calls of one
+    shape on different streams get different workspaces, so they may run
+    concurrently (calls on one stream are ordered by the stream)."""
+    stream = torch.cuda.current_stream(device).cuda_stream
+    cache = plan.__dict__.setdefault("_ws", {})
+    ws = cache.get((device, stream))
+    if ws is None:
         ws = torch.empty(plan.workspace_bytes + 256, dtype=torch.uint8, device=device)
         pad = (-ws.data_ptr()) % 256
         ws = ws[pad:pad + plan.workspace_bytes]
-        plan._ws = ws
+        cache[(device, stream)] = ws
     return ws
 
 
@@ -278,19 +292,52 @@ def attention_prepared(prep: Prepared, with_repair=None, out=None, weights="expc
     return out
 
 
-def debug_pcodes(prep: Prepared, b: int, h: int, with_codes: bool = True, weights="expcast"):
-    """Bytes the attention kernel wrote for every (query, key) of one (b, h)
-    (None when with_codes is False), the running row max it used per key
-    tile, and the output."""
+class Dump:
+    """What the attention kernel computed for the listed query rows of one
+    (b, h) (oc_attn_debug_pcodes). Arrays are device tensors, row i of each
+    belonging to rows[i]; fields not asked for are None.
+      codes   u8  [n, S]       ExpCast bytes of the main loop
+      m_used  i32 [n, nT]      running row max used for each key tile, by tile
+      scores  f32 [n, S]       raw FP8 MFMA sums <q_hat, k_hat>
+      rcodes  u8  [n, n_sel]   repair-pass bytes (with_repair)
+      out_f32 f32 [n, 128]     output rows before BF16 rounding
+      out     bf16, the full output tensor; only (b, h) is written"""
+
+    def __init__(self, **kw):
+        self.__dict__.update(kw)
+
+
+def debug_pcodes(prep: Prepared, b: int, h: int, rows=None, codes=True, m_used=True, scores=False, out_f32=False,
+                 with_repair=False, weights="expcast") -> Dump:
+    """Run the attention kernel's parity-aid variant on a prepared workspace
+    for one (b, h) and record its bytes, running maxima, raw scores, repair
+    bytes and fp32 output rows for the given query rows (default: all)."""
     _set_weights(prep.plan, weights)
     B, S, H, _ = prep.shape
+    dev = prep.device
     nT = prep.plan.layout.n_ktiles
-    codes = torch.zeros((S, S), dtype=torch.uint8, device=prep.device) if with_codes else None
-    m_used = torch.full((S, nT), -(1 << 30), dtype=torch.int32, device=prep.device)
-    out = torch.zeros(prep.shape, dtype=torch.bfloat16, device=prep.device)
-    _check(_lib.oc_attn_debug_pcodes(prep.plan.handle, _ptr(prep.ws), prep.ws.numel(), b, h, _ptr(codes),
-                                     _ptr(m_used), _ptr(out), _stream(prep.device)), "oc_attn_debug_pcodes")
-    return codes, m_used, out
+    rows_t = torch.arange(S, dtype=torch.int32, device=dev) if rows is None else \
+        torch.as_tensor(rows, dtype=torch.int32).to(dev)
+    n = rows_t.numel()
+    n_sel = 0
+    if with_repair:
+        if prep.budget is None:
+            raise OcAttnError(OC_ERR_NOT_PREPARED, "with_repair needs a workspace from prepare_v_repair")
+        n_sel = prep.n_sel
+    d = Dump(rows=rows_t,
+             codes=torch.zeros((n, S), dtype=torch.uint8, device=dev) if codes else None,
+             m_used=torch.full((n, nT), -(1 << 30), dtype=torch.int32, device=dev) if m_used else None,
+             scores=torch.full((n, S), float("nan"), dtype=torch.float32, device=dev) if scores else None,
+             rcodes=torch.zeros((n, max(n_sel, 1)), dtype=torch.uint8, device=dev) if with_repair else None,
+             out_f32=torch.full((n, 128), float("nan"), dtype=torch.float32, device=dev) if out_f32 else None,
+             out=torch.zeros(prep.shape, dtype=torch.bfloat16, device=dev))
+    _check(_lib.oc_attn_debug_pcodes(prep.plan.handle, _ptr(prep.ws), prep.ws.numel(), b, h, _ptr(rows_t), n,
+                                     int(bool(with_repair)), _ptr(d.codes), _ptr(d.m_used), _ptr(d.scores),
+                                     _ptr(d.rcodes), _ptr(d.out_f32), _ptr(d.out), _stream(dev)),
+           "oc_attn_debug_pcodes")
+    if d.rcodes is not None:
+        d.rcodes = d.rcodes[:, :n_sel]
+    return d
 
 
 def flops(B, S, H, D=128):
@@ -298,5 +345,5 @@ def flops(B, S, H, D=128):
     return 4.0 * B * S * S * H * D
 
 
-__all__ = ["attention", "attention_v_repair", "prepare", "prepare_v_repair", "attention_prepared", "debug_pcodes",
+__all__ = ["attention", "attention_v_repair", "prepare", "prepare_v_repair", "attention_prepared", "debug_pcodes", "Dump",
            "Plan", "Prepared", "OcAttnError", "flops", "load_library", "EXPORTS", "LIB_PATH", "WEIGHTS"]

@@ -215,7 +215,10 @@ __device__ __forceinline__ void qk_tile(const uint8_t* kt, const v8i (&qop)[QBW]
 
 // O^T += V^T P^T and (ROWSUM) L += 1 * P^T for one tile, with the same
 // read-ahead. With PRE the first RA operands were read by the caller (pre).
-template <bool ROWSUM = true, bool PRE = false>
+// ASM false issues the same MFMA through the compiler builtin: the code-dump
+// variant of the kernel (a parity aid that spills registers) uses it, so that
+// the compiler sees the accumulators and separates its spill code from them.
+template <bool ROWSUM = true, bool PRE = false, bool ASM = true>
 __device__ __forceinline__ void pv_tile(const uint8_t* vt, v8i (&P)[QBW], const int (&sb)[QBW], int one,
                                         v4f (&O)[QBW][8], v4f (&L)[QBW], int lane, const v8i& ones,
                                         const v8i* pre = nullptr) {
@@ -227,7 +230,10 @@ __device__ __forceinline__ void pv_tile(const uint8_t* vt, v8i (&P)[QBW], const 
   for (int n = 0; n < 8; ++n) {
     if (n + RA < 8) vop[n + RA] = lds_operand(vt, n + RA, lane);
 #pragma unroll
-    for (int qb = 0; qb < QBW; ++qb) mfma_f8_sb_acc(O[qb][n], vop[n], P[qb], one, sb[qb]);
+    for (int qb = 0; qb < QBW; ++qb) {
+      if (ASM) mfma_f8_sb_acc(O[qb][n], vop[n], P[qb], one, sb[qb]);
+      else O[qb][n] = mfma_f8_sb(vop[n], P[qb], O[qb][n], sb[qb]);
+    }
   }
   if (ROWSUM) {
 #pragma unroll
@@ -418,7 +424,7 @@ template <bool DUMP, bool EXPP>
 __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], float aq8, float skj, float& Mv,
                                              float& Mr, int (&sb)[QBW], v4f (&O)[QBW][8], v4f (&L)[QBW],
                                              v4f (&C)[QBW], int j, bool masked, const AttnArgs& a, int g,
-                                             int qrow0) {
+                                             const int (&dslot)[QBW]) {
   if (masked) {
     // keys beyond S in the last (ragged) tile take no part in max or sums.
     // The empty asm makes lim opaque, so that the 32 compares stay in this
@@ -441,15 +447,18 @@ __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], fl
   const float mv = row_max_pair(lane_max32(S[0]), lane_max32(S[1]));
   const float Mn = fmax_p(Mv, __builtin_ceilf(aqs8 * mv));
   if (__builtin_amdgcn_ballot_w64(Mn > Mv) != 0) {
-    // O and L stay in the frame of a reference max Mr <= M: the bytes of this
-    // tile weigh 2^(Mn - Mr) there, a factor the PV and row-sum MFMAs apply as
-    // the E8M0 scale of their P operand. O and L are rescaled (exactly, by a
+    // O and L stay in the frame of a reference max Mr: the bytes of this tile
+    // weigh 2^(Mn - Mr) there, a factor the PV and row-sum MFMAs apply as the
+    // E8M0 scale of their P operand. O and L are rescaled (exactly, by a
     // power of two) only where the frame would fall more than FRAME_DRIFT
-    // binades behind, which includes the first tile.
+    // binades behind. The running max starts at -inf and the frame at 0, so
+    // on the first tile the frame moves to the tile's max unless that lies in
+    // [0, FRAME_DRIFT] (O and L are still zero then); from there on
+    // Mr <= Mv.
     float e = Mn - Mr;
-    if (__builtin_amdgcn_ballot_w64(e > FRAME_DRIFT) != 0) {
+    if (__builtin_amdgcn_ballot_w64(e > FRAME_DRIFT || e < 0.0f) != 0) {
       ofence(O);
-      const bool re = e > FRAME_DRIFT;
+      const bool re = e > FRAME_DRIFT || e < 0.0f;
       float d0, d1;   // exponent change of each block (<= 0)
       spread_pair(re ? -e : 0.0f, d0, d1);
       const int d[QBW] = {(int)d0, (int)d1};
@@ -491,21 +500,36 @@ __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], fl
     spread_pair(Mn, mq[0], mq[1]);
 #pragma unroll
     for (int qb = 0; qb < QBW; ++qb) {
-      const int qrow = qrow0 + 16 * qb;
-      if (qrow < a.S) {
-        if (a.dump_codes != nullptr) {
+      const int slot = dslot[qb];
+      if (slot >= 0) {
 #pragma unroll
-          for (int kb = 0; kb < 8; ++kb)
+        for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int key = j * KTILE + 16 * kb + 4 * g + r;
-              if (key < a.S) a.dump_codes[(int64_t)qrow * a.S + key] = (uint8_t)((uint32_t)P[qb][kb] >> (8 * r));
+          for (int r = 0; r < 4; ++r) {
+            const int key = j * KTILE + 16 * kb + 4 * g + r;
+            if (key < a.S) {
+              const int64_t at = (int64_t)slot * a.S + key;
+              if (a.dump_codes != nullptr) a.dump_codes[at] = (uint8_t)((uint32_t)P[qb][kb] >> (8 * r));
+              if (a.dump_scores != nullptr) a.dump_scores[at] = S[qb][kb][r];
             }
-        }
-        if (g == 0) a.dump_m[(int64_t)qrow * a.nT + j] = (int32_t)mq[qb];
+          }
+        if (g == 0 && a.dump_m != nullptr) a.dump_m[(int64_t)slot * a.nT + j] = (int32_t)mq[qb];
       }
     }
   }
+}
+
+// Row-list slot of a query row in the dump (the first index i with
+// rows[i] == row), or -1. The search only ever narrows [lo, hi), so it ends
+// within log2(n) + 1 steps and stays inside the list whatever it holds.
+__device__ inline int dump_slot(const AttnArgs& a, int row) {
+  int lo = 0, hi = a.n_dump;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a.dump_rows[mid] < row) lo = mid + 1;
+    else hi = mid;
+  }
+  return (lo < a.n_dump && a.dump_rows[lo] == row) ? lo : -1;
 }
 
 // the two parts of the tile loop (see the kernel)
@@ -582,6 +606,12 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   const int q0 = qt * BQ + wv * QBW * 16;
   const int qrow0 = q0 + l16;
   const int nT = a.nT;
+  int dslot[QBW] = {-1, -1};   // dump slots of this lane's two query rows
+  if (DUMP) {
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb)
+      if (qrow0 + 16 * qb < a.S) dslot[qb] = dump_slot(a, qrow0 + 16 * qb);
+  }
 
   // Q^T operands stay in registers for the whole loop
   v8i qop[QBW];
@@ -604,9 +634,9 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   asm volatile("" : "+v"(ones));
   v4f O[QBW][8], L[QBW], S[QBW][8];
   v8i P[QBW];
-  float Mv = -16384.0f;            // running max per block by row parity (see expcast_tile)
+  float Mv = -__builtin_inff();    // running max per block by row parity (see expcast_tile)
   v4f C[QBW];                      // V-Smooth: row sums of the current batch of sixteen tiles
-  float Mr = -16384.0f;            // reference max of O and L, same layout
+  float Mr = 0.0f;                 // reference max of O and L, same layout
   int sb[QBW] = {127, 127};        // E8M0 scale of the P operand: 2^(M - Mr)
   int one = 127;                   // the V operand's unit scale, in a register
   asm volatile("" : "+v"(one));
@@ -685,9 +715,9 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
     if (ld_mu) load_means(mofs + ((s + 2) & (MU_NBUF - 1)) * MU_SLOT, mu_ptr(s + 2), voff_mu);
     const float skj = skp[j];
     if (!GB) {
-      expcast_tile<DUMP, EXPP>(S, P, aq8, skj, Mv, Mr, sb, O, L, C, j, j == last_masked, a, g, qrow0);
+      expcast_tile<DUMP, EXPP>(S, P, aq8, skj, Mv, Mr, sb, O, L, C, j, j == last_masked, a, g, dslot);
       if (VSMOOTH) vsmooth_tile(P, sb, C, l16 == (s & 15) ? 127 : 0, ones);
-      pv_tile<!VSMOOTH, true>(vbuf + b0 * TILE_BYTES, P, sb, one, O, L, lane, ones, pre);
+      pv_tile<!VSMOOTH, true, !DUMP>(vbuf + b0 * TILE_BYTES, P, sb, one, O, L, lane, ones, pre);
       if (VSMOOTH && ((s & 15) == 15 || s + 1 == nT)) {
         ofence(O);
         vsmooth_flush(mubuf, s, vinv, O, L, C, g, l16);
@@ -697,7 +727,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
     } else {
       __builtin_amdgcn_s_setprio(2);
       qk_tile<KPRE>(kbuf + b0 * TILE_BYTES, qop, S, lane, pre);
-      if (s > 0) pv_tile<!VSMOOTH, true>(vbuf + bm1 * TILE_BYTES, P, sb, one, O, L, lane, ones, bpre);
+      if (s > 0) pv_tile<!VSMOOTH, true, !DUMP>(vbuf + bm1 * TILE_BYTES, P, sb, one, O, L, lane, ones, bpre);
       // the batch that ended with tile s-1 (before ExpCast(s) may re-anchor)
       if (VSMOOTH && s > 0 && ((s - 1) & 15) == 15) {
         ofence(O);
@@ -705,7 +735,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
         ofence(O);
       }
       __builtin_amdgcn_s_setprio(0);
-      expcast_tile<DUMP, EXPP>(S, P, aq8, skj, Mv, Mr, sb, O, L, C, j, j == last_masked, a, g, qrow0);
+      expcast_tile<DUMP, EXPP>(S, P, aq8, skj, Mv, Mr, sb, O, L, C, j, j == last_masked, a, g, dslot);
       if (VSMOOTH) vsmooth_tile(P, sb, C, l16 == (s & 15) ? 127 : 0, ones);
       // K step s+1 and V step s have been in LDS since the last barrier: the
       // first operands of the next QK and PV arrive before the next one
@@ -736,7 +766,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
     for (; s < nT; ++s) iteration(s, bool_tag<true>{}, bool_tag<false>{});
   }
   if (group_b) {
-    pv_tile<!VSMOOTH, true>(vbuf + ((nT - 1) & (NBUF - 1)) * TILE_BYTES, P, sb, one, O, L, lane, ones, bpre);
+    pv_tile<!VSMOOTH, true, !DUMP>(vbuf + ((nT - 1) & (NBUF - 1)) * TILE_BYTES, P, sb, one, O, L, lane, ones, bpre);
     if (VSMOOTH) {
       ofence(O);
       vsmooth_flush(mubuf, nT - 1, vinv, O, L, C, g, l16);
@@ -760,19 +790,22 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0);
 
-  float scale = a.sv[2 * bh];
-  if (REPAIR && a.n_sel > 0) {
-    // residual pass over the selected value tokens, with the final row max
-    // and without touching L: O = sv*sum P v_hat + sr*sum P r_hat
-    const float sr = a.sr[2 * bh];
-    const float rs = scale / sr;
-    float M[QBW];   // final running max of each block, in every lane
-    spread_pair(Mv, M[0], M[1]);
+  // Repair pass over the selected value tokens, with the final row max and
+  // without touching L. Its sum R = sum_sel P r_hat has an accumulator of
+  // its own (the scores' registers are free by now), so that the output
+  // (sv*O + sr*R)/L needs no ratio of the two scales, which can leave the
+  // fp32 range when the selected residuals are tiny against V.
+  v4f R[QBW][8];
+  const bool rep = REPAIR && a.n_sel > 0;
+  if (REPAIR) {
 #pragma unroll
     for (int qb = 0; qb < QBW; ++qb)
 #pragma unroll
-      for (int n = 0; n < 8; ++n) O[qb][n] *= rs;
-    scale = sr;
+      for (int n = 0; n < 8; ++n) R[qb][n] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  if (rep) {
+    float M[QBW];   // final running max of each block, in every lane
+    spread_pair(Mv, M[0], M[1]);
     const int nslot = a.n_sel_tiles * KTILE;
     const uint8_t* ksb = a.kselpack + (int64_t)bh * a.n_sel_tiles * TILE_BYTES;
     const uint8_t* rsb = a.rpack + (int64_t)bh * a.n_sel_tiles * TILE_BYTES;
@@ -814,29 +847,43 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
             }
           }
           P[qb][kb] = (int)w;
+          if (DUMP && a.dump_rcodes != nullptr && dslot[qb] >= 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (live[r])
+                a.dump_rcodes[(int64_t)dslot[qb] * a.n_sel + ts * KTILE + 16 * kb + 4 * g + r] = (uint8_t)(w >> (8 * r));
+          }
         }
       }
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
         const v8i rop = lds_operand(vbuf, n, lane);
 #pragma unroll
-        for (int qb = 0; qb < QBW; ++qb) O[qb][n] = mfma_f8(rop, P[qb], O[qb][n]);
+        for (int qb = 0; qb < QBW; ++qb) R[qb][n] = mfma_f8(rop, P[qb], R[qb][n]);
       }
     }
   }
 
-  // ---- epilogue: out = O * scale / L, BF16
+  // ---- epilogue: out = (sv*O + sr*R) / L, BF16
+  const float sv = a.sv[2 * bh];
+  const float sr = rep ? a.sr[2 * bh] : 0.0f;
 #pragma unroll
   for (int qb = 0; qb < QBW; ++qb) {
     const int qrow = q0 + 16 * qb + l16;
     if (qrow >= a.S) continue;
-    const float f = scale / L[qb][0];
+    const float fv = sv / L[qb][0], fr = sr / L[qb][0];
     uint16_t* orow = a.out + (((int64_t)b * a.S + qrow) * a.H + h) * HEAD_DIM + 4 * g;
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
-      const uint32_t lo = f32_to_bf16(O[qb][n][0] * f) | (f32_to_bf16(O[qb][n][1] * f) << 16);
-      const uint32_t hi = f32_to_bf16(O[qb][n][2] * f) | (f32_to_bf16(O[qb][n][3] * f) << 16);
+      float y[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[r] = REPAIR ? __builtin_fmaf(R[qb][n][r], fr, O[qb][n][r] * fv) : O[qb][n][r] * fv;
+      const uint32_t lo = f32_to_bf16(y[0]) | (f32_to_bf16(y[1]) << 16);
+      const uint32_t hi = f32_to_bf16(y[2]) | (f32_to_bf16(y[3]) << 16);
       *reinterpret_cast<uint2*>(orow + 16 * n) = make_uint2(lo, hi);
+      if (DUMP && a.dump_out32 != nullptr && dslot[qb] >= 0)
+        *reinterpret_cast<float4*>(a.dump_out32 + (int64_t)dslot[qb] * HEAD_DIM + 16 * n + 4 * g) =
+            make_float4(y[0], y[1], y[2], y[3]);
     }
   }
 }
@@ -857,7 +904,7 @@ static hipError_t launch_one(const AttnArgs& a, dim3 grid, hipStream_t st) {
 
 template <bool EXPP, bool VSMOOTH>
 static hipError_t launch_variant(const AttnArgs& a, bool repair, bool dump, dim3 grid, hipStream_t st) {
-  if (dump) return launch_one<false, true, EXPP, VSMOOTH>(a, grid, st);
+  if (dump) return repair ? launch_one<true, true, EXPP, VSMOOTH>(a, grid, st) : launch_one<false, true, EXPP, VSMOOTH>(a, grid, st);
   return repair ? launch_one<true, false, EXPP, VSMOOTH>(a, grid, st) : launch_one<false, false, EXPP, VSMOOTH>(a, grid, st);
 }
 

@@ -60,7 +60,7 @@ struct oc_attn_plan {
   int gvsmooth = -1;
   // the workspaces this plan prepared most recently, with their repair count
   // (-1: prepared without repair)
-  static constexpr int NPREP = 8;
+  static constexpr int NPREP = 64;
   const void* prepared_ws[NPREP] = {};
   int prepared_nsel[NPREP] = {};
   int prepared_vs[NPREP] = {};
@@ -435,18 +435,32 @@ oc_status oc_attn_forward_prepared(oc_attn_plan* p, const void* ws, size_t ws_by
 }
 
 oc_status oc_attn_debug_pcodes(oc_attn_plan* p, const void* ws, size_t ws_bytes, int32_t b, int32_t h,
-                               uint8_t* codes, int32_t* m_used, void* out, void* stream) {
-  if (!p || !ws || !m_used || !out) return OC_ERR_INVALID_ARGUMENT;
+                               const int32_t* rows, int32_t n_rows, int32_t with_repair, uint8_t* codes,
+                               int32_t* m_used, float* scores, uint8_t* rcodes, float* out_f32, void* out,
+                               void* stream) {
+  if (!p || !ws || !out || !rows || ((uintptr_t)ws & 255u)) return OC_ERR_INVALID_ARGUMENT;
   if (b < 0 || b >= p->d.B || h < 0 || h >= p->d.H) return OC_ERR_INVALID_ARGUMENT;
-  if (codes && p->d.S > 8192) return OC_ERR_UNSUPPORTED;
+  if (n_rows < 1 || n_rows > p->d.S) return OC_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)rows & 3u) || ((uintptr_t)m_used & 3u) || ((uintptr_t)scores & 3u) || ((uintptr_t)out_f32 & 15u))
+    return OC_ERR_INVALID_ARGUMENT;
   if (ws_bytes < p->L.total_bytes) return OC_ERR_WORKSPACE_TOO_SMALL;
-  if (p->prepared_state(ws) == -2) return OC_ERR_NOT_PREPARED;
-  AttnArgs a = attn_args(p, ws, out, 0);
+  oc_status s = check_out(p, out, nullptr, 0, ws, ws_bytes);
+  if (s != OC_OK) return s;
+  const int state = p->prepared_state(ws);
+  if (state == -2) return OC_ERR_NOT_PREPARED;
+  if (with_repair && state < 0) return OC_ERR_NOT_PREPARED;
+  const int n_sel = with_repair ? state : 0;
+  AttnArgs a = attn_args(p, ws, out, n_sel);
+  a.dump_rows = rows;
+  a.n_dump = n_rows;
   a.dump_codes = codes;
   a.dump_m = m_used;
+  a.dump_scores = scores;
+  a.dump_rcodes = n_sel > 0 ? rcodes : nullptr;
+  a.dump_out32 = out_f32;
   a.dump_b = b;
   a.dump_h = h;
-  const hipError_t e = launch_attention(a, false, true, (hipStream_t)stream);
+  const hipError_t e = launch_attention(a, n_sel > 0, true, (hipStream_t)stream);
   return e == hipSuccess ? OC_OK : hip_fail(e);
 }
 

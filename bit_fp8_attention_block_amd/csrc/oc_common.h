@@ -84,9 +84,13 @@ __device__ inline uint32_t f32_to_bf16(float f) {
 }
 
 // Quantization scales from a block amax: s = amax/448, inv = 448/amax
-// (correctly rounded fp32 divisions); an all-zero block gets (1, 1).
+// (correctly rounded fp32 divisions). A block whose amax is below 2^-100, an
+// all-zero block included, gets (1, 1): every element then rounds to code 0,
+// and 448/amax, which leaves the fp32 range below about 1.3e-36, is never
+// formed. From 2^-100 up both quotients are normal numbers.
+constexpr float SCALE_FLOOR = 0x1p-100f;
 __device__ inline void quant_scales(float amax, float& s, float& inv) {
-  if (amax == 0.0f) { s = 1.0f; inv = 1.0f; return; }
+  if (amax < SCALE_FLOOR) { s = 1.0f; inv = 1.0f; return; }
   s = __fdiv_rn(amax, E4M3_MAX);
   inv = __fdiv_rn(E4M3_MAX, amax);
 }

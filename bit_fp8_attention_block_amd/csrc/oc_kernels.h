@@ -54,8 +54,14 @@ struct AttnArgs {
   int order;                   // 0: from the middle of the key window outwards, 1: ascending
   int exp_path;                // 0: ExpCast bytes; 1: exp2 + FP32->E4M3 cast (comparison path)
   const uint16_t* vmu;         // V-Smooth: [B][H][nT][128] bf16 block means (nullptr: off)
-  uint8_t* dump_codes;         // debug: [S][S] bytes for one (b, h)
-  int32_t* dump_m;             // debug: [S][nT]
+  // parity aid (the DUMP variant only): one (b, h), the listed query rows
+  const int32_t* dump_rows;    // [n_dump] ascending query rows
+  int n_dump;
+  uint8_t* dump_codes;         // [n_dump][S] main-loop bytes (or nullptr)
+  int32_t* dump_m;             // [n_dump][nT] running max per key tile (or nullptr)
+  float* dump_scores;          // [n_dump][S] raw MFMA sums <q_hat, k_hat> (or nullptr)
+  uint8_t* dump_rcodes;        // [n_dump][n_sel] repair-pass bytes (or nullptr)
+  float* dump_out32;           // [n_dump][128] fp32 output before BF16 rounding (or nullptr)
   int dump_b, dump_h;
 };
 

@@ -334,7 +334,11 @@ __global__ __launch_bounds__(256) void prep_v_kernel(PrepArgs a) {
 
   if (REPAIR) {
     // residual r = v - sv*dec(code) in fp32 (two roundings, no fusion);
-    // energy = sum of r^2 over the 128 channels in float64
+    // energy = sum of r^2 over the 128 channels in float64, added pairwise in
+    // channel order: each square is exact, a four-level tree adds this
+    // thread's 16 channels (an aligned block of the channel order), and the
+    // xor exchanges over the 8 threads of the token are the tree's top three
+    // levels (a + b == b + a, so every thread ends with the same bits)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const uint32_t w[8] = {lo[r].x, lo[r].y, lo[r].z, lo[r].w, hi[r].x, hi[r].y, hi[r].z, hi[r].w};
@@ -347,14 +351,19 @@ __global__ __launch_bounds__(256) void prep_v_kernel(PrepArgs a) {
         const v2f hi2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[j], true);
         dec[4 * j] = lo2[0]; dec[4 * j + 1] = lo2[1]; dec[4 * j + 2] = hi2[0]; dec[4 * j + 3] = hi2[1];
       }
-      double e = 0.0;
+      double e2[16];
 #pragma unroll
       for (int c = 0; c < 16; ++c) {
         const float x = __fsub_rn(bits_to_f32<FP16>((w[c >> 1] >> (16 * (c & 1))) & 0xFFFFu), mu[c]);
         const float t = __fmul_rn(sv, dec[c]);
         const double d = (double)__fsub_rn(x, t);
-        e = __builtin_fma(d, d, e);
+        e2[c] = d * d;
       }
+#pragma unroll
+      for (int n = 8; n >= 1; n >>= 1)
+#pragma unroll
+        for (int i = 0; i < n; ++i) e2[i] = e2[2 * i] + e2[2 * i + 1];
+      double e = e2[0];
       e += __shfl_xor(e, 1, 64);
       e += __shfl_xor(e, 2, 64);
       e += __shfl_xor(e, 4, 64);

@@ -26,6 +26,8 @@
  *   Q/K: per 128-token block, s = amax/448 (fp32). The code is E4M3(q * 448/amax),
  *        round to nearest even, saturating.
  *   V:   one scale per head, sv = amax/448, same rounding.
+ *   A block, head or repair set whose amax is below 2^-100 (an all-zero one
+ *   included) takes s = 1: every code is then 0 and those values count as 0.
  *   x_ij  = tau*log2(e) * sq_i * sk_j * <q_hat_i, k_hat_j>
  *   M_i   = ceil(max_j x_ij)                      (bit-aligned row max)
  *   c_ij  = clamp(rne(8*(x_ij - M_i) + 119.65), 0, 126)   (E4M3 byte of 256*2^(x-M))
@@ -65,6 +67,11 @@
  *   A failing HIP call gives OC_ERR_HIP. oc_attn_last_hip_error() then
  *   returns the hipError_t of the calling thread's last failure.
  * NaN or Inf inputs are not supported; the output for them is undefined.
+ * Otherwise the output is finite wherever the method's own result is, with
+ * one exception in the V-Smooth option (oc_attn_plan_set_v_smoothing): when
+ * a head's block means exceed its smoothed residuals by more than about
+ * 2^60 (for example means near 1e20 beside residuals near 1e-25), the mean
+ * term can overflow the fp32 accumulator.
  */
 #ifndef OC_ATTN_H
 #define OC_ATTN_H
@@ -204,21 +211,39 @@ oc_status oc_attn_forward_v_repair(oc_attn_plan* plan, const void* q, const void
                                    double budget, void* out, void* ws, size_t ws_bytes, void* stream);
 
 /* Attention only, on a workspace this plan prepared earlier (kernel-alone
- * timing; the plan remembers its 8 most recently prepared workspaces).
+ * timing; the plan remembers its 64 most recently prepared workspaces).
  * with_repair != 0 requires the workspace to come from
  * oc_attn_prepare_v_repair; its repair set is then applied. */
 oc_status oc_attn_forward_prepared(oc_attn_plan* plan, const void* ws, size_t ws_bytes, void* out,
                                    int with_repair, void* stream);
 
-/* Parity aid: run the attention kernel (without repair) on the prepared
- * workspace for the one (b, h) pair and dump, for every query row < S, the
- * running row max it used for each key tile (m_used: device i32
- * [S][n_ktiles], indexed by tile number) and, if codes is not NULL, the
- * ExpCast byte it wrote for every key (codes: device u8 [S][S]; only for
- * S <= 8192, larger S gives OC_ERR_UNSUPPORTED). out receives the normal
- * output for that (b, h). */
+/* Parity aid: run the attention kernel on the prepared workspace for the
+ * one (b, h) pair, every query tile of it, and record what it computed for
+ * the listed query rows. out receives the normal BF16 output of that (b, h)
+ * (the same bits the attention calls write there); other (b, h) pairs of out
+ * are left alone.
+ *   rows      device i32 [n_rows], ascending and distinct query rows
+ *             (1 <= n_rows <= S; entries outside [0, S) are never matched,
+ *             and an unsorted list leaves some rows unrecorded)
+ *   with_repair  != 0: the workspace must come from oc_attn_prepare_v_repair,
+ *             and its repair pass runs (else OC_ERR_NOT_PREPARED)
+ * Each of the following device buffers may be NULL (not recorded); slot i
+ * holds the row rows[i]:
+ *   codes     u8  [n_rows][S]       the ExpCast byte of every key
+ *   m_used    i32 [n_rows][n_ktiles] the running row max each key tile's
+ *                                   bytes were written against, by tile
+ *   scores    f32 [n_rows][S]       the raw FP8 MFMA sum <q_hat_i, k_hat_j>
+ *                                   (codes as E4M3 values, before any scale)
+ *   rcodes    u8  [n_rows][n_sel]   with_repair: the byte of every selected
+ *                                   token in the repair pass (slot order)
+ *   out_f32   f32 [n_rows][128]     the output row before BF16 rounding
+ *                                   (16-byte aligned)
+ * Same validation as oc_attn_forward_prepared, plus b, h and n_rows ranges;
+ * misaligned buffers give OC_ERR_INVALID_ARGUMENT. */
 oc_status oc_attn_debug_pcodes(oc_attn_plan* plan, const void* ws, size_t ws_bytes, int32_t b, int32_t h,
-                               uint8_t* codes, int32_t* m_used, void* out, void* stream);
+                               const int32_t* rows, int32_t n_rows, int32_t with_repair, uint8_t* codes,
+                               int32_t* m_used, float* scores, uint8_t* rcodes, float* out_f32, void* out,
+                               void* stream);
 
 /* Static description of a status code. */
 const char* oc_attn_status_string(oc_status status);

@@ -1,6 +1,7 @@
 """Test-side helpers for the GPU parity tests: read the prepared tensors out
-of a workspace (restating the pack layouts documented in include/oc_attn.h)
-and run the oracle on the same inputs."""
+of a workspace (restating the pack layouts documented in include/oc_attn.h),
+read the attention kernel's parity-aid dump, validate its running-max
+decisions, and run the oracle on the same inputs."""
 from __future__ import annotations
 
 import math
@@ -142,3 +143,122 @@ def oracle_rows(q, k, v, b, h, rows, budget=0.0, tau=None, order="mid", m_trace=
 
 def out_rows(out, b, h, rows):
     return out[b, :, h].float().cpu().numpy()[np.asarray(rows)].astype(np.float64)
+
+
+TOL = 5e-3
+# oracle byte path -> the kernel's name for it
+KERNEL_WEIGHTS = {"expcast": "expcast", "exp_cast": "exp_fp8"}
+
+
+def _oc():
+    import bit_fp8_attention_block_amd as oc
+    return oc
+
+
+def logit_error_bound(ph, rows, tau):
+    """Worst-case difference between the kernel's log2-logit and the exact one:
+    the FP8 MFMA's summation error, bounded by 2^-10 of the largest possible
+    product max|q| * max|k| (test_gpu_mfma_precision checks that bound on the
+    hardware, on adversarial and workload data), plus fp32 rounding of the
+    sum (128 * 2^-24 * sum |products|) and of the three scale products and
+    the FMA (a few ulp of the logit)."""
+    qd = np.abs(oracle.decode(ph.qc[np.asarray(rows)]))
+    kd = np.abs(oracle.decode(ph.kc))
+    sqr = ph.sq[np.asarray(rows) // 128].astype(np.float64)
+    skk = ph.sk[np.arange(ph.S) // 128].astype(np.float64)
+    scale = (tau / math.log(2)) * (sqr[:, None] * skk[None, :])
+    mag = scale * (qd @ kd.T)
+    top = scale * np.outer(qd.max(axis=1), kd.max(axis=1))
+    return mag * (128 * 2.0 ** -24) + mag * 2.0 ** -20 + top * 2.0 ** -10
+
+
+def check_max_trace(trace, x, bound, order="mid"):
+    """Validate every running-max decision the kernel made for these rows.
+
+    trace[i, t] is the max the kernel wrote tile t's bytes against (by tile
+    number); x the exact log2-logits, bound their worst-case kernel error.
+    Visiting the tiles in the kernel's order, each entry must be
+    max(previous entry, ceil(m)) for some tile max m the kernel could have
+    seen: m between the largest (x - bound) and the largest (x + bound) of
+    the tile. So entries never decrease, equal the exact decision wherever
+    the tile's largest logit is further than the bound from an integer, and
+    elsewhere may differ only toward the side such a rounding reaches.
+    Returns the number of rows with at least one such tie-broken entry."""
+    n, nT = trace.shape
+    S = x.shape[1]
+    tiles = oracle.key_tile_order(nT) if order == "mid" else list(range(nT))
+    prev = np.full(n, -np.inf)
+    tie = np.zeros(n, dtype=bool)
+    for t in tiles:
+        sl = slice(t * 128, min(S, t * 128 + 128))
+        lo = np.ceil((x[:, sl] - bound[:, sl]).max(axis=1))
+        hi = np.ceil((x[:, sl] + bound[:, sl]).max(axis=1))
+        exact = np.maximum(prev, np.ceil(x[:, sl].max(axis=1)))
+        got = trace[:, t].astype(np.float64)
+        ok = (got >= np.maximum(prev, lo)) & (got <= np.maximum(prev, hi))
+        bad = np.nonzero(~ok)[0]
+        assert len(bad) == 0, (f"tile {t}: row {bad[0]} kernel max {got[bad[0]]}, previous {prev[bad[0]]}, "
+                               f"allowed [{max(prev[bad[0]], lo[bad[0]])}, {max(prev[bad[0]], hi[bad[0]])}]")
+        tie |= got != exact
+        prev = got
+    return int(tie.sum())
+
+
+def kernel_dump(prep, b, h, rows, out=None, weights="expcast", with_repair=False, **want):
+    """The parity-aid dump for one (b, h) and the given rows, as numpy arrays.
+    With `out` (the output of the production call on the same inputs), the
+    dump variant's own output for that (b, h) must equal it bit for bit: it
+    then took the same decisions as the kernel whose output is compared."""
+    oc = _oc()
+    d = oc.debug_pcodes(prep, b, h, rows=np.asarray(rows), weights=KERNEL_WEIGHTS.get(weights, weights),
+                        with_repair=with_repair, **want)
+    torch.cuda.synchronize()
+    if out is not None:
+        assert torch.equal(d.out[b, :, h], out[b, :, h]), "dump variant and production kernel disagree"
+    for f in ("codes", "m_used", "scores", "rcodes", "out_f32"):
+        t = getattr(d, f)
+        if t is not None:
+            setattr(d, f, t.cpu().numpy())
+    return d
+
+
+def validated_trace(q, k, v, prep, b, h, rows, out=None, budget=0.0, tau=None, order="mid", weights="expcast",
+                    k_smooth=False, v_smooth=False):
+    """The kernel's running-max decisions for `rows` of (b, h), after
+    check_max_trace has accepted every one of them; (trace, tie rows)."""
+    d = kernel_dump(prep, b, h, rows, out=out, weights=weights, with_repair=budget > 0, codes=False)
+    own = oracle_rows(q, k, v, b, h, rows, budget=budget, tau=tau, order=order, weights=weights,
+                      k_smooth=k_smooth, v_smooth=v_smooth)
+    t = tau if tau else 1 / math.sqrt(128)
+    x = oracle.log2_logits(own["ph"], rows, t)
+    ties = check_max_trace(d.m_used, x, logit_error_bound(own["ph"], rows, t), order)
+    return d.m_used, ties
+
+
+def compare(q, k, v, out, pairs, rows, budget=0.0, tol=TOL, label="", order="mid", prep=None, weights="expcast",
+            k_smooth=False, v_smooth=False, tau=None):
+    """rel-L2 of the kernel's rows against the single-pass oracle. With a
+    prepared workspace (of the same inputs and options), the oracle replays
+    the running-max decisions the kernel made, each validated first by
+    check_max_trace, and the dump's output must equal `out` bit for bit."""
+    errs, two = [], []
+    nflip = 0
+    for b, h in pairs:
+        m_trace = None
+        if prep is not None:
+            m_trace, ties = validated_trace(q, k, v, prep, b, h, rows, out=out, budget=budget, tau=tau, order=order,
+                                            weights=weights, k_smooth=k_smooth, v_smooth=v_smooth)
+            nflip += ties
+        r = oracle_rows(q, k, v, b, h, rows, budget=budget, tau=tau, order=order, m_trace=m_trace, weights=weights,
+                        k_smooth=k_smooth, v_smooth=v_smooth)
+        got = out_rows(out, b, h, rows)
+        e = oracle.rel_l2(got, r["out"])
+        errs.append(e)
+        r2 = oracle.expcast_attention_head(head64(q, b, h), head64(k, b, h), head64(v, b, h), tau=tau, rows=rows,
+                                           ph=r["ph"], weights=weights)
+        two.append(oracle.rel_l2(got, r2["out"]))
+        assert np.isfinite(got).all()
+        assert e <= tol, (label, b, h, e)
+    log(f"  {label}: rel-L2 vs oracle (single-pass form) max {max(errs):.2e}; vs two-pass form max {max(two):.2e}"
+        + (f"; rows with a tie-broken max {nflip}" if prep is not None else ""))
+    return errs

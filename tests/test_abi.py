@@ -132,22 +132,25 @@ def test_forward_argument_errors_before_any_hip_call():
     assert lib.oc_attn_forward_prepared(p, vp(ws), ws_bytes, vp(out), 0, None) == oc.OC_ERR_NOT_PREPARED
     assert lib.oc_attn_forward_prepared(p, vp(ws), ws_bytes, vp(out), 1, None) == oc.OC_ERR_NOT_PREPARED
     assert lib.oc_attn_forward_prepared(p, vp(ws), 10, vp(out), 0, None) == oc.OC_ERR_WORKSPACE_TOO_SMALL
-    codes, m = FAKE + (16 << 30), FAKE + (20 << 30)
-    assert lib.oc_attn_debug_pcodes(p, vp(ws), ws_bytes, 0, 0, vp(codes), vp(m), vp(out), None) == \
-        oc.OC_ERR_NOT_PREPARED
-    assert lib.oc_attn_debug_pcodes(p, vp(ws), ws_bytes, 0, 9, vp(codes), vp(m), vp(out), None) == \
-        oc.OC_ERR_INVALID_ARGUMENT
+    rows, codes, m = FAKE + (15 << 30), FAKE + (16 << 30), FAKE + (20 << 30)
+    dbg = lib.oc_attn_debug_pcodes
+
+    def dump(b=0, h=0, rws=rows, n=10, rep=0, cd=codes, f32=None, o=out, w=ws, nbytes=ws_bytes):
+        return dbg(p, vp(w), nbytes, b, h, vp(rws), n, rep, vp(cd), vp(m), None, None, vp(f32), vp(o), None)
+    assert dump() == oc.OC_ERR_NOT_PREPARED
+    assert dump(rep=1) == oc.OC_ERR_NOT_PREPARED
+    assert dump(h=9) == oc.OC_ERR_INVALID_ARGUMENT
+    assert dump(b=-1) == oc.OC_ERR_INVALID_ARGUMENT
+    assert dump(n=0) == oc.OC_ERR_INVALID_ARGUMENT
+    assert dump(n=1001) == oc.OC_ERR_INVALID_ARGUMENT          # more rows than S
+    assert dump(rws=None) == oc.OC_ERR_INVALID_ARGUMENT
+    assert dump(rws=rows + 2) == oc.OC_ERR_INVALID_ARGUMENT      # misaligned row list
+    assert dump(f32=FAKE + (24 << 30) + 4) == oc.OC_ERR_INVALID_ARGUMENT
+    assert dump(o=None) == oc.OC_ERR_INVALID_ARGUMENT
+    assert dump(o=ws) == oc.OC_ERR_INVALID_ARGUMENT             # output overlapping the workspace
+    assert dump(nbytes=100) == oc.OC_ERR_WORKSPACE_TOO_SMALL
     lib.oc_attn_plan_destroy(p)
     lib.oc_attn_plan_destroy(None)
-
-
-def test_debug_dump_limited_to_small_s():
-    st, p = create(make_desc(S=9000, H=1))
-    n = ctypes.c_size_t()
-    lib.oc_attn_workspace_size(p, ctypes.byref(n))
-    assert lib.oc_attn_debug_pcodes(p, vp(FAKE), n.value, 0, 0, vp(FAKE + (1 << 34)), vp(FAKE + (1 << 35)),
-                                    vp(FAKE + (1 << 36)), None) == oc.OC_ERR_UNSUPPORTED
-    lib.oc_attn_plan_destroy(p)
 
 
 def test_status_strings():

@@ -19,91 +19,44 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import head64, log, oracle_rows, out_rows
+from gpu_util import (KERNEL_WEIGHTS, TOL, _oc, check_max_trace, compare, head64, kernel_dump,  # noqa: F401
+                      log, logit_error_bound, oracle_rows, out_rows)
 
 pytestmark = pytest.mark.gpu
 
-TOL = 5e-3
-# oracle byte path -> the kernel's name for it
-KERNEL_WEIGHTS = {"expcast": "expcast", "exp_cast": "exp_fp8"}
+# helpers shared by the GPU parity tests (also imported from here by older call sites)
+_compare = compare
 
 
-def _oc():
-    import bit_fp8_attention_block_amd as oc
-    return oc
-
-
-def logit_error_bound(ph, rows, tau):
-    """Worst-case difference between the kernel's logit and the exact one.
-    The FP8 MFMA does not sum its 128 products to fp32 accuracy: measured on
-    gfx950 against exact sums (8192 trials of random codes, and of small
-    codes beside one dominant product), its error stayed within 2^-11.3 of
-    the largest product's magnitude; the bound allows 2^-10 of the largest
-    possible product, max|q| * max|k|. On top of that, fp32 rounding of the
-    sum (128 * 2^-24 * sum |products|) and of the three scale products and
-    the FMA (a few ulp of the logit)."""
-    qd = np.abs(oracle.decode(ph.qc[np.asarray(rows)]))
-    kd = np.abs(oracle.decode(ph.kc))
-    sqr = ph.sq[np.asarray(rows) // 128].astype(np.float64)
-    skk = ph.sk[np.arange(ph.S) // 128].astype(np.float64)
-    scale = (tau / math.log(2)) * (sqr[:, None] * skk[None, :])
-    mag = scale * (qd @ kd.T)
-    top = scale * np.outer(qd.max(axis=1), kd.max(axis=1))
-    return mag * (128 * 2.0 ** -24) + mag * 2.0 ** -20 + top * 2.0 ** -10
-
-
-def check_max_trace(kernel_trace, own, x, bound, order="mid"):
-    """The kernel's running max per tile must match the oracle's, except where
-    a tile's largest logit lies within the kernel's logit error bound of an
-    integer:
-    there the first divergence must be exactly one, at such a tie."""
-    nT = kernel_trace.shape[1]
-    tiles = oracle.key_tile_order(nT) if order == "mid" else list(range(nT))
-    S = x.shape[1]
-    bad_rows = np.nonzero((kernel_trace != own).any(axis=1))[0]
-    for i in bad_rows:
-        for t in tiles:
-            if kernel_trace[i, t] != own[i, t]:
-                sl = slice(t * 128, min(S, t * 128 + 128))
-                xm = x[i, sl].max()
-                assert abs(int(kernel_trace[i, t]) - int(own[i, t])) == 1, (i, t)
-                assert abs(xm - round(xm)) <= bound[i, sl].max(), (i, t, xm, bound[i, sl].max())
-                break
-    return len(bad_rows)
-
-
-def _compare(q, k, v, out, pairs, rows, budget=0.0, tol=TOL, label="", order="mid", prep=None, weights="expcast",
-             k_smooth=False, v_smooth=False, tau=None):
-    """rel-L2 of the kernel's rows against the single-pass oracle. With a
-    prepared workspace, the oracle replays the running-max decisions the
-    kernel made (read back through the debug dump), after checking that each
-    of them agrees with the oracle's own or is a rounding tie at an integer."""
-    errs, two = [], []
-    nflip = 0
-    for b, h in pairs:
-        m_trace = None
-        if prep is not None:
-            oc = _oc()
-            _, m_used, _ = oc.debug_pcodes(prep, b, h, with_codes=False, weights=KERNEL_WEIGHTS[weights])
-            m_trace = m_used[torch.as_tensor(rows, device=m_used.device)].cpu().numpy()
-            own = oracle_rows(q, k, v, b, h, rows, budget=budget, tau=tau, order=order, weights=weights,
-                              k_smooth=k_smooth, v_smooth=v_smooth)
-            t = tau if tau else 1 / math.sqrt(128)
-            x = oracle.log2_logits(own["ph"], rows, t)
-            nflip += check_max_trace(m_trace, own["m_trace"], x, logit_error_bound(own["ph"], rows, t), order)
-        r = oracle_rows(q, k, v, b, h, rows, budget=budget, tau=tau, order=order, m_trace=m_trace, weights=weights,
-                        k_smooth=k_smooth, v_smooth=v_smooth)
-        got = out_rows(out, b, h, rows)
-        e = oracle.rel_l2(got, r["out"])
-        errs.append(e)
-        r2 = oracle.expcast_attention_head(head64(q, b, h), head64(k, b, h), head64(v, b, h), tau=tau, rows=rows,
-                                           ph=r["ph"], weights=weights)
-        two.append(oracle.rel_l2(got, r2["out"]))
-        assert np.isfinite(got).all()
-        assert e <= tol, (label, b, h, e)
-    log(f"  {label}: rel-L2 vs oracle (single-pass form) max {max(errs):.2e}; vs two-pass form max {max(two):.2e}"
-        + (f"; rows with a tie-broken max {nflip}" if prep is not None else ""))
-    return errs
+def check_bytes(q, k, v, prep, b, h, rows, out=None, weights="expcast", tau=None, label=""):
+    """The kernel's bytes for the given rows of (b, h) against the oracle's
+    bytes for the same logits and the running max the kernel used for each
+    key (validated first): at least 99.9% equal, never more than one code
+    apart. The final running max is the bit-aligned row max up to a tie
+    within the logit error bound. Returns the dump."""
+    tau = tau or 1 / math.sqrt(128)
+    S = q.shape[1]
+    d = kernel_dump(prep, b, h, rows, out=out, weights=weights)
+    ph = oracle.prepare_head(head64(q, b, h), head64(k, b, h), head64(v, b, h))
+    x = oracle.log2_logits(ph, rows, tau)
+    bound = logit_error_bound(ph, rows, tau)
+    ties = check_max_trace(d.m_used, x, bound)
+    Mk = d.m_used[:, np.arange(S) // 128]              # running max used for each (row, key)
+    want = (oracle.expcast_codes if weights == "expcast" else oracle.exp_cast_codes)(x, Mk)
+    diff = np.abs(d.codes.astype(int) - want.astype(int))
+    agree = (diff == 0).mean()
+    log(f"  {label} (b={b},h={h}) {len(rows)} rows: byte agreement {agree:.6f}, max diff {diff.max()}, "
+        f"tie-broken rows {ties}")
+    assert agree >= 0.999 and diff.max() <= 1, (agree, diff.max())
+    Mfinal = d.m_used.max(axis=1)
+    Mo = oracle.bitaligned_row_max(x)
+    xmax = x.max(axis=1)
+    for i in np.nonzero(Mfinal != Mo)[0]:
+        gap = abs(xmax[i] - round(xmax[i]))
+        log(f"  row {rows[i]}: kernel M {Mfinal[i]} oracle M {Mo[i]} (max logit {xmax[i]:.9f})")
+        assert abs(int(Mfinal[i]) - int(Mo[i])) == 1 and gap <= bound[i].max()
+    d.x, d.ph, d.agree = x, ph, agree
+    return d
 
 
 @pytest.mark.parametrize("case", ["s1024_h2", "ragged300", "s130", "biased2048"])
@@ -119,38 +72,38 @@ def test_expcast_bytes_match_oracle(case):
     else:
         q, k, v = workloads.make_inputs("s73397_h56", device="cuda", S=2048, H=2)
     B, S, H, _ = q.shape
+    out = oc.attention(q, k, v)
     prep = oc.prepare(q, k, v)
-    tau = 1 / math.sqrt(128)
     for b in range(B):
         for h in range(H):
-            codes, m_used, out = oc.debug_pcodes(prep, b, h)
-            torch.cuda.synchronize()
-            codes, m_used = codes.cpu().numpy(), m_used.cpu().numpy()
-            ph = oracle.prepare_head(head64(q, b, h), head64(k, b, h), head64(v, b, h))
-            x = oracle.log2_logits(ph, np.arange(S), tau)
-            tiles = np.arange(S) // 128
-            Mk = m_used[:, tiles]                      # running max used for each (row, key)
-            assert (Mk > -(1 << 29)).all(), "every tile must have been visited"
-            want = oracle.expcast_codes(x, Mk)
-            diff = np.abs(codes.astype(int) - want.astype(int))
-            agree = (diff == 0).mean()
-            log(f"  (b={b},h={h}) byte agreement {agree:.6f}, max diff {diff.max()}")
-            assert agree >= 0.999 and diff.max() <= 1
-            # the final running max is the bit-aligned row max, except where the
-            # row's largest logit lies within the logit error bound of an integer
-            Mfinal = m_used.max(axis=1)
-            Mo = oracle.bitaligned_row_max(x)
-            bad = np.nonzero(Mfinal != Mo)[0]
-            xmax = x.max(axis=1)
-            bound = logit_error_bound(ph, np.arange(S), tau) if len(bad) else None
-            for i in bad:
-                gap = abs(xmax[i] - round(xmax[i]))
-                log(f"  row {i}: kernel M {Mfinal[i]} oracle M {Mo[i]} (max logit {xmax[i]:.9f})")
-                assert abs(int(Mfinal[i]) - int(Mo[i])) == 1 and gap <= bound[i].max()
-            # the dumped output equals the oracle too
-            r = oracle.expcast_attention_online(head64(q, b, h), head64(k, b, h), head64(v, b, h), ph=ph)
+            d = check_bytes(q, k, v, prep, b, h, np.arange(S), out=out, label=case)
+            r = oracle.expcast_attention_online(head64(q, b, h), head64(k, b, h), head64(v, b, h), ph=d.ph,
+                                                m_trace=d.m_used)
             e = oracle.rel_l2(out_rows(out, b, h, np.arange(S)), r["out"])
             assert e <= TOL, e
+
+
+@pytest.mark.parametrize("name,rows_per_head,pairs", [
+    ("s8192_h8", 1024, "all"),
+    ("s32768_h14", 128, [(0, 0), (0, 6), (0, 13)]),
+    ("s73397_h56", 96, [(0, 0), (0, 27), (0, 55)]),
+    ("b2_s70000_h40_fp16", 96, [(0, 0), (1, 39)]),
+])
+def test_expcast_bytes_match_oracle_at_full_size(name, rows_per_head, pairs):
+    """Byte parity on the full workloads, in the launch configuration the
+    benchmark times: every key of sampled query rows (the ragged tail
+    included), on every head of s8192_h8 and on heads across the others."""
+    oc = _oc()
+    w = workloads.WORKLOADS[name]
+    log(f"[bytes full size] {name} B={w.B} S={w.S} H={w.H}")
+    q, k, v = workloads.make_inputs(name, device="cuda")
+    out = oc.attention(q, k, v)
+    prep = oc.prepare(q, k, v)
+    rows = np.array(workloads.sample_rows(w.S, rows_per_head, seed=w.seed))
+    if pairs == "all":
+        pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
+    for b, h in pairs:
+        check_bytes(q, k, v, prep, b, h, rows, out=out, label=name)
 
 
 @pytest.mark.parametrize("name,rows_per_head,pairs", [
@@ -324,3 +277,59 @@ def test_traversal_orders_match_their_oracle():
                  order="mid" if order == "0" else "ascending", label=f"order {order}")
     d = (outs[0] - outs[1]).norm() / outs[1].norm()
     log(f"  mid-window vs ascending rel-L2 {d.item():.2e}")
+
+
+def test_very_negative_logits_stay_finite():
+    """Rows whose log2-logits all lie near -1.6e5, far below any finite
+    starting value a running max could be given: every key is the same
+    vector, so each row's weights are uniform and its output is the mean of
+    the dequantized values, for the kernel as for the oracle."""
+    oc = _oc()
+    S, H = 600, 2
+    g = torch.Generator().manual_seed(41)
+    w = torch.randint(0, 2, (H, 128), generator=g).float() * 2 - 1                # +-1 per channel
+    flips = (torch.rand(S, H, 128, generator=g) < 0.05).float() * -2 + 1
+    q = (-100.0 * w[None] * flips)[None]                                           # q.k = -1e4 * (128 - 2 flips)
+    k = (100.0 * w)[None, None].expand(1, S, H, 128).contiguous()
+    v = torch.randn(1, S, H, 128, generator=g)
+    q, k, v = (t.to(torch.bfloat16).cuda() for t in (q, k, v))
+    log("[range] very negative logits")
+    out = oc.attention(q, k, v)
+    prep = oc.prepare(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    for h in range(H):
+        ph = oracle.prepare_head(head64(q, 0, h), head64(k, 0, h), head64(v, 0, h))
+        x = oracle.log2_logits(ph, np.arange(0, S, 37), 1 / math.sqrt(128))
+        assert x.max() < -1e5
+        mean = float(ph.sv) * oracle.decode(ph.vc).mean(axis=0)
+        got = out_rows(out, 0, h, np.arange(S))
+        e = oracle.rel_l2(got, np.tile(mean, (S, 1)))
+        log(f"  h={h}: rel-L2 vs the mean value {e:.2e}")
+        assert e <= TOL
+    compare(q, k, v, out, [(0, 0), (0, 1)], np.arange(0, S, 5), label="very negative logits", prep=prep)
+
+
+def test_repair_with_tiny_residuals_stays_finite():
+    """Values exactly on the E4M3 grid of their head scale (residual 0)
+    except one element of 2^-90: the selected residuals are ~2^-99 of the
+    head's value scale. The repaired output must stay finite and match the
+    oracle; a kernel that multiplied its accumulator by that ratio would
+    overflow fp32."""
+    oc = _oc()
+    S, H, budget = 700, 1, 0.01
+    g = torch.Generator().manual_seed(42)
+    grid = torch.tensor(oracle.VALUES[:127], dtype=torch.float32)
+    v = grid[torch.randint(0, 127, (1, S, H, 128), generator=g)] * (torch.randint(0, 2, (1, S, H, 128), generator=g) * 2 - 1)
+    v[0, 3, 0, 0] = 448.0                  # head amax 448: scale 1, every value exact
+    v[0, 250, 0, 7] = 2.0 ** -90           # rounds to code 0: the one non-zero residual
+    q, k, _ = workloads.make_inputs("s8192_h8", S=S, H=H)
+    q, k, v = q.cuda(), k.cuda(), v.to(torch.bfloat16).cuda()
+    log("[range] tiny residuals")
+    out = oc.attention_v_repair(q, k, v, budget)
+    prep = oc.prepare_v_repair(q, k, v, budget)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    rp = oracle.prepare_head(head64(q, 0, 0), head64(k, 0, 0), head64(v, 0, 0), budget).repair
+    assert 250 in rp.sel and float(rp.sr) < 2.0 ** -90 / 400
+    compare(q, k, v, out, [(0, 0)], np.arange(0, S, 3), budget=budget, label="tiny residuals", prep=prep)

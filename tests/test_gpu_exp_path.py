@@ -3,8 +3,6 @@ then the FP32 -> E4M3 cast; weights="exp_fp8") against the oracle's
 exp_cast_codes path: bytes at least 99.9% equal and never more than one code
 apart (v_exp_f32 is within 1 ulp of the correctly rounded fp32 weight, and
 the logits are fp32), outputs within the same 5e-3 relative L2."""
-import math
-
 import numpy as np
 import pytest
 import torch
@@ -12,7 +10,7 @@ import torch
 import oracle
 import workloads
 from gpu_util import head64, log, out_rows
-from test_gpu_attention import TOL, _compare
+from test_gpu_attention import TOL, _compare, check_bytes
 
 pytestmark = pytest.mark.gpu
 
@@ -33,29 +31,18 @@ def test_exp_path_bytes_match_oracle(case):
     else:
         q, k, v = workloads.random_qkv(1, 130, 1, seed=4, device="cuda", scale=2.0)
     B, S, H, _ = q.shape
+    out = oc.attention(q, k, v, weights="exp_fp8")
     prep = oc.prepare(q, k, v)
-    tau = 1 / math.sqrt(128)
     for b in range(B):
         for h in range(H):
-            codes, m_used, out = oc.debug_pcodes(prep, b, h, weights="exp_fp8")
-            torch.cuda.synchronize()
-            codes, m_used = codes.cpu().numpy(), m_used.cpu().numpy()
-            ph = oracle.prepare_head(head64(q, b, h), head64(k, b, h), head64(v, b, h))
-            x = oracle.log2_logits(ph, np.arange(S), tau)
-            Mk = m_used[:, np.arange(S) // 128]
-            assert (Mk > -(1 << 29)).all()
-            want = oracle.exp_cast_codes(x, Mk)
-            diff = np.abs(codes.astype(int) - want.astype(int))
-            agree = (diff == 0).mean()
+            d = check_bytes(q, k, v, prep, b, h, np.arange(S), out=out, weights="exp_cast", label=case)
             # the two byte paths are different maps: about 80% equal, one apart elsewhere
-            expcast = oracle.expcast_codes(x, Mk)
-            other = (codes == expcast).mean()
-            log(f"  (b={b},h={h}) byte agreement {agree:.6f}, max diff {diff.max()}; "
-                f"equal to ExpCast bytes {other:.3f}")
-            assert agree >= 0.999 and diff.max() <= 1
+            Mk = d.m_used[:, np.arange(S) // 128]
+            other = (d.codes == oracle.expcast_codes(d.x, Mk)).mean()
+            log(f"  (b={b},h={h}) equal to ExpCast bytes {other:.3f}")
             assert other < 0.95
-            r = oracle.expcast_attention_online(head64(q, b, h), head64(k, b, h), head64(v, b, h), ph=ph,
-                                                weights="exp_cast", m_trace=m_used)
+            r = oracle.expcast_attention_online(head64(q, b, h), head64(k, b, h), head64(v, b, h), ph=d.ph,
+                                                weights="exp_cast", m_trace=d.m_used)
             e = oracle.rel_l2(out_rows(out, b, h, np.arange(S)), r["out"])
             assert e <= TOL, e
 

@@ -75,3 +75,36 @@ def test_prepare_extreme_ranges():
     prep = oc.prepare(q, k, v)
     torch.cuda.synchronize()
     _check_prepared(q, k, v, prep)
+
+
+def test_prepare_tiny_blocks_take_the_unit_scale():
+    """Blocks (and a whole head of V) whose amax lies below 2^-100 take the
+    unit scale and codes 0 (0x80 for negative values), while a block whose
+    amax is 2^-100 itself and one just above take their regular scales."""
+    import bit_fp8_attention_block_amd as oc
+    log("[prepare] tiny blocks")
+    S, H = 640, 2
+    g = torch.Generator().manual_seed(12)
+    x = torch.randn(1, S, H, 128, generator=g)
+    q = x.clone()
+    q[:, 0:128] *= 2.0 ** -110          # below the floor: unit scale
+    q[:, 128:256] *= 2.0 ** -102        # |x| up to ~2^-100: straddles the floor, some blocks each way
+    k = x.flip(1).clone()
+    k[:, 256:384] *= 2.0 ** -120
+    blk = k[:, 384:512]
+    k[:, 384:512] = blk / blk.abs().amax(dim=(0, 1, 3), keepdim=True) * 2.0 ** -100   # amax exactly 2^-100: regular
+    v = torch.randn(1, S, H, 128, generator=g)
+    v[:, :, 1] *= 2.0 ** -115           # the whole of head 1 is below the floor
+    q, k, v = (t.to(torch.bfloat16).cuda() for t in (q, k, v))
+    prep = oc.prepare(q, k, v)
+    out = oc.attention(q, k, v)
+    torch.cuda.synchronize()
+    _check_prepared(q, k, v, prep)
+    w = WsView(prep)
+    assert np.all(w.sq(0, 0)[0] == 1.0) and np.all(w.sk(0, 0)[2] == 1.0)
+    assert w.sk(0, 0)[3] != 1.0
+    assert w.sv(0, 1)[0] == 1.0 and not (w.vcodes(0, 1) & 0x7F).any()
+    assert (w.vcodes(0, 1) == 0x80).any()
+    # head 1's values all count as zero: its output is zero
+    assert torch.isfinite(out.float()).all()
+    assert not out[0, :, 1].float().abs().max().item()
