@@ -485,7 +485,13 @@ __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], fl
   float b[QBW];   // the FMA's addend per block, in every lane
   // (ExpCast: a and b over 65535, for bytes_expcast's unorm16 conversion)
   spread_pair(EXPP ? 8.0f - Mn : __builtin_fmaf(-8.0f / 65535.0f, Mn, EXPCAST_C / 65535.0f), b[0], b[1]);
-  const float aqs = aqs8 * (8.0f / 65535.0f);
+  // a/65535 is the same in every lane of the wave: it goes to an SGPR, so the
+  // 64 FMAs of a tile read two VGPRs each instead of three. (The empty
+  // statement hides that the value is uniform, which would let the compiler
+  // drop the readfirstlane and keep it in a VGPR.)
+  float aqs_v = aqs8 * (8.0f / 65535.0f);
+  asm volatile("" : "+v"(aqs_v));
+  const float aqs = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, aqs_v)));
 #pragma unroll
   for (int kb = 0; kb < 8; ++kb)
 #pragma unroll

@@ -333,3 +333,48 @@ def test_repair_with_tiny_residuals_stays_finite():
     rp = oracle.prepare_head(head64(q, 0, 0), head64(k, 0, 0), head64(v, 0, 0), budget).repair
     assert 250 in rp.sel and float(rp.sr) < 2.0 ** -90 / 400
     compare(q, k, v, out, [(0, 0)], np.arange(0, S, 3), budget=budget, label="tiny residuals", prep=prep)
+
+
+@pytest.mark.parametrize("name,rows_per_head,pairs", [
+    ("s32768_h14", 192, [(0, 0), (0, 7), (0, 13)]),
+    ("s73397_h56", 64, [(0, 0), (0, 55)]),
+])
+def test_error_decomposition(name, rows_per_head, pairs):
+    """Where the kernel's distance from the oracle comes from, on the
+    sampled rows the workload test uses:
+      bytes    the output the oracle's arithmetic (float64) gives from the
+               kernel's own bytes and running maxima, against the oracle:
+               the effect of bytes one code away (fp32 logits);
+      fp32     the kernel's fp32 output before BF16 rounding, against that
+               same float64 output from its bytes: the FP8 MFMA and fp32
+               accumulation of P V and of the row sums;
+      bf16     the BF16 output against the kernel's fp32 output.
+    Each part stays below the tolerance, and they add up (in quadrature or
+    less) to the total."""
+    oc = _oc()
+    w = workloads.WORKLOADS[name]
+    log(f"[error parts] {name}")
+    q, k, v = workloads.make_inputs(name, device="cuda")
+    out = oc.attention(q, k, v)
+    prep = oc.prepare(q, k, v)
+    rows = np.array(workloads.sample_rows(w.S, rows_per_head, seed=w.seed))
+    S = w.S
+    for b, h in pairs:
+        d = kernel_dump(prep, b, h, rows, out=out, out_f32=True)
+        r = oracle_rows(q, k, v, b, h, rows, m_trace=d.m_used)
+        ph = r["ph"]
+        x = oracle.log2_logits(ph, rows, 1 / math.sqrt(128))
+        check_max_trace(d.m_used, x, logit_error_bound(ph, rows, 1 / math.sqrt(128)))
+        Mfin = d.m_used.max(axis=1)
+        frame = np.exp2(d.m_used[:, np.arange(S) // 128] - Mfin[:, None])       # each key's tile weight in the final frame
+        P = oracle.VALUES[d.codes] * frame
+        from_bytes = float(ph.sv) * (P @ oracle.decode(ph.vc)) / P.sum(axis=1, keepdims=True)
+        e_bytes = oracle.rel_l2(from_bytes, r["out"])
+        e_fp32 = oracle.rel_l2(d.out_f32, from_bytes)
+        e_bf16 = oracle.rel_l2(out_rows(out, b, h, rows), d.out_f32)
+        e_tot = oracle.rel_l2(out_rows(out, b, h, rows), r["out"])
+        per_row = np.linalg.norm(from_bytes - r["out"], axis=1) / np.linalg.norm(r["out"], axis=1)
+        log(f"  ({b},{h}) total {e_tot:.2e} = bytes {e_bytes:.2e} (worst row {per_row.max():.2e}) + fp32 {e_fp32:.2e} "
+            f"+ bf16 {e_bf16:.2e}")
+        assert max(e_bytes, e_fp32, e_bf16) <= TOL
+        assert e_tot <= e_bytes + e_fp32 + e_bf16 + 1e-12
