@@ -20,6 +20,7 @@ SDPA on the same GPU for comparison. Progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -120,19 +121,34 @@ def cpu_baseline(q, k, v, w, rows_n):
             "seconds": t}
 
 
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16 MFMA
+
+
 def bf16_comparator(q, k, v, steps):
-    """torch SDPA on BF16 [B,H,S,D] tensors (flash / memory-efficient backends
-    only; the math backend would materialize S x S)."""
+    """torch SDPA on BF16 [B,H,S,D] tensors, each fused backend timed on its
+    own: the flash backend with torch's ROCm library preference set to
+    AOTriton and to composable_kernel (torch falls back to another library
+    where the preferred one lacks the operation), and the memory-efficient
+    backend (the math backend would materialize S x S). Returns
+    {backend: ms} for the backends that ran."""
     from torch.nn.attention import SDPBackend, sdpa_kernel
     qt, kt, vt = (x.to(torch.bfloat16).transpose(1, 2).contiguous() for x in (q, k, v))
-    try:
-        with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
-            fn = lambda: torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)  # noqa: E731
-            ms, _ = timed_calls(fn, steps, 1)
-        return ms
-    except Exception as e:  # no fused BF16 backend for this shape
-        log(f"bf16 comparator unavailable: {e}")
-        return None
+    fn = lambda: torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)  # noqa: E731
+    res = {}
+    before = torch.backends.cuda.preferred_rocm_fa_library()
+    for name, backend, lib in (("flash/aotriton", SDPBackend.FLASH_ATTENTION, "aotriton"),
+                               ("flash/ck", SDPBackend.FLASH_ATTENTION, "ck"),
+                               ("efficient", SDPBackend.EFFICIENT_ATTENTION, None)):
+        try:
+            if lib is not None:
+                torch.backends.cuda.preferred_rocm_fa_library(lib)
+            with sdpa_kernel([backend]):
+                res[name], _ = timed_calls(fn, steps, 1)
+        except Exception as e:  # backend not built for this shape or this torch
+            log(f"bf16 comparator {name} unavailable: {str(e)[:200]}")
+        finally:
+            torch.backends.cuda.preferred_rocm_fa_library(before)
+    return res
 
 
 def main():
@@ -149,6 +165,7 @@ def main():
     ap.add_argument("--kernel-only", action="store_true", help="time only the attention kernel (for profiling)")
     ap.add_argument("--weights", default="expcast", choices=("expcast", "exp_fp8"),
                     help="byte path of the kernel timed by --kernel-only")
+    ap.add_argument("--prepare-only", action="store_true", help="time only the prepare step (for profiling)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -177,6 +194,20 @@ def main():
     q, k, v = workloads.make_inputs(w, device=dev)
     torch.cuda.synchronize()
     flop = oc.flops(w.B, w.S, w.H)
+
+    if args.prepare_only:
+        plan = oc.get_plan(q, None, args.budget)
+        ws = oc._workspace(plan, dev)
+        if args.budget > 0:
+            fn = lambda: oc._lib.oc_attn_prepare_v_repair(  # noqa: E731
+                plan.handle, oc._ptr(q), oc._ptr(k), oc._ptr(v), ctypes.c_double(args.budget), oc._ptr(ws),
+                ws.numel(), oc._stream(dev))
+        else:
+            fn = lambda: oc._lib.oc_attn_prepare(plan.handle, oc._ptr(q), oc._ptr(k), oc._ptr(v),  # noqa: E731
+                                                 oc._ptr(ws), ws.numel(), oc._stream(dev))
+        p_ms, _ = timed_calls(fn, args.steps, args.warmup)
+        print(json.dumps({"prepare_ms": p_ms, "budget": args.budget}))
+        return
 
     # kernel alone on a prepared workspace (the roofline kernel)
     prep = oc.prepare_v_repair(q, k, v, max(args.budget, args.repair_budget))
@@ -213,11 +244,13 @@ def main():
         step()
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    log("[bench] full call and repaired full call, round-robin")
-    fm = interleaved_calls({"full": step,
-                            "repair": lambda: oc.attention_v_repair(q, k, v, args.repair_budget, out=out)},
-                           args.steps, 1)
-    full_ev_ms, rep_ms = fm["full"], fm["repair"]
+    log("[bench] full call and repaired full calls (budgets 0.005, 0.01, 0.02), round-robin")
+    rep_budgets = sorted({args.repair_budget, 0.005, 0.01, 0.02})
+    calls = {"full": step}
+    for rb in rep_budgets:
+        calls[f"repair_{rb:g}"] = (lambda b_: lambda: oc.attention_v_repair(q, k, v, b_, out=out))(rb)
+    fm = interleaved_calls(calls, args.steps, 1)
+    full_ev_ms, rep_ms = fm["full"], fm[f"repair_{args.repair_budget:g}"]
     # prepare alone (the captured graph), HBM-bound
     plan = oc.get_plan(q, None, 0.0)
     ws = oc._workspace(plan, dev)
@@ -230,7 +263,9 @@ def main():
     oc._lib.oc_attn_plan_set_k_smoothing(plan.handle, 0)
     in_bytes = 3 * 2 * w.B * w.S * w.H * 128
     prep_bytes = in_bytes + in_bytes // 2 + (in_bytes // 3)   # read q,k,v + V again; write 3 FP8 tensors
-    sdpa_ms = None if args.no_comparator else bf16_comparator(q, k, v, max(2, min(args.steps, 3)))
+    sdpa = {} if args.no_comparator else bf16_comparator(q, k, v, max(2, min(args.steps, 3)))
+    sdpa_best = min(sdpa, key=sdpa.get) if sdpa else None
+    sdpa_ms = sdpa[sdpa_best] if sdpa else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -272,7 +307,14 @@ def main():
         "prepare_k_smooth_ms": round(pks_ms, 4),
         "full_call_repair_ms": round(rep_ms, 4),
         "repair_budget_measured": args.repair_budget,
+        "full_call_repair_ms_by_budget": {f"{rb:g}": round(fm[f"repair_{rb:g}"], 4) for rb in rep_budgets},
+        "repair_overhead_pct_by_budget": {f"{rb:g}": round(100.0 * (fm[f"repair_{rb:g}"] / full_ev_ms - 1.0), 2)
+                                          for rb in rep_budgets},
         "bf16_sdpa_ms": None if sdpa_ms is None else round(sdpa_ms, 3),
+        "bf16_sdpa_backend": sdpa_best,
+        "bf16_sdpa_ms_by_backend": {n: round(t, 3) for n, t in sdpa.items()},
+        "bf16_sdpa_tflops": None if sdpa_ms is None else round(flop / sdpa_ms / 1e9, 1),
+        "bf16_sdpa_frac_of_bf16_peak": None if sdpa_ms is None else round(flop / sdpa_ms / 1e9 / BF16_PEAK_TFLOPS, 4),
         "speedup_vs_bf16_sdpa": None if sdpa_ms is None else round(sdpa_ms / ms_per_step, 3),
     }
     print(json.dumps(rec), flush=True)
