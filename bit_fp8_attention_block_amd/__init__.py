@@ -56,7 +56,10 @@ class WsLayout(ctypes.Structure):
 EXPORTS = ("oc_attn_plan_create", "oc_attn_plan_destroy", "oc_attn_workspace_size", "oc_attn_workspace_layout",
            "oc_attn_prepare", "oc_attn_forward", "oc_attn_prepare_v_repair", "oc_attn_forward_v_repair",
            "oc_attn_forward_prepared", "oc_attn_debug_pcodes", "oc_attn_status_string", "oc_attn_last_hip_error",
-           "oc_attn_plan_set_weights", "oc_attn_plan_set_k_smoothing", "oc_attn_plan_set_v_smoothing")
+           "oc_attn_plan_set_weights", "oc_attn_plan_set_k_smoothing", "oc_attn_plan_set_v_smoothing",
+           "oc_attn_forward_v_repair_noalloc")
+# workspace capacity of oc_attn_forward_v_repair_noalloc (per GPU)
+NOALLOC_WORKSPACE_BYTES = 64 << 20
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -78,6 +81,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.oc_attn_prepare_v_repair.argtypes = [P, VP, VP, VP, D, VP, SZ, VP]
     lib.oc_attn_forward_v_repair.argtypes = [P, VP, VP, VP, D, VP, VP, SZ, VP]
     lib.oc_attn_forward_prepared.argtypes = [P, VP, SZ, VP, ctypes.c_int, VP]
+    lib.oc_attn_forward_v_repair_noalloc.argtypes = [P, VP, VP, VP, D, VP, VP]
     lib.oc_attn_debug_pcodes.argtypes = [P, VP, SZ, I32, I32, VP, I32, I32, VP, VP, VP, VP, VP, VP, VP]
     lib.oc_attn_status_string.argtypes = [st]
     lib.oc_attn_status_string.restype = ctypes.c_char_p
@@ -86,7 +90,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                  "oc_attn_plan_set_v_smoothing",
                  "oc_attn_workspace_size", "oc_attn_workspace_layout", "oc_attn_prepare",
                  "oc_attn_forward", "oc_attn_prepare_v_repair", "oc_attn_forward_v_repair",
-                 "oc_attn_forward_prepared", "oc_attn_debug_pcodes"):
+                 "oc_attn_forward_prepared", "oc_attn_debug_pcodes", "oc_attn_forward_v_repair_noalloc"):
         getattr(lib, name).restype = st
     del I64
     return lib
@@ -280,6 +284,23 @@ def attention_v_repair(q, k, v, budget, softmax_scale=None, out=None, weights="e
     return out.squeeze(0) if squeeze else out
 
 
+def attention_noalloc(q, k, v, budget=0.0, softmax_scale=None, out=None, weights="expcast"):
+    """Full call (with repair when budget > 0) on the library's own workspace
+    array instead of a torch-allocated one (oc_attn_forward_v_repair_noalloc):
+    for shapes whose workspace fits NOALLOC_WORKSPACE_BYTES. Calls that
+    overlap in time on one GPU race on that array."""
+    q, k, v, squeeze = _canon(q, k, v)
+    plan = get_plan(q, softmax_scale, budget)
+    _set_weights(plan, weights)
+    _set_smoothing(plan, False, False)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(_lib.oc_attn_forward_v_repair_noalloc(plan.handle, _ptr(q), _ptr(k), _ptr(v), ctypes.c_double(budget),
+                                                     _ptr(out), _stream(q.device)), "oc_attn_forward_v_repair_noalloc")
+    return out.squeeze(0) if squeeze else out
+
+
 def attention_prepared(prep: Prepared, with_repair=None, out=None, weights="expcast"):
     """Attention only, on a workspace filled by prepare / prepare_v_repair."""
     _set_weights(prep.plan, weights)
@@ -345,5 +366,5 @@ def flops(B, S, H, D=128):
     return 4.0 * B * S * S * H * D
 
 
-__all__ = ["attention", "attention_v_repair", "prepare", "prepare_v_repair", "attention_prepared", "debug_pcodes", "Dump",
+__all__ = ["attention", "attention_v_repair", "attention_noalloc", "prepare", "prepare_v_repair", "attention_prepared", "debug_pcodes", "Dump",
            "Plan", "Prepared", "OcAttnError", "flops", "load_library", "EXPORTS", "LIB_PATH", "WEIGHTS"]

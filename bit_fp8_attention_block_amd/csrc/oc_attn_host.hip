@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/oc_attn.h"
 #include "oc_common.h"
@@ -309,6 +310,38 @@ static oc_status run_attention(oc_attn_plan* p, const void* ws, void* out, int n
   return e == hipSuccess ? OC_OK : hip_fail(e);
 }
 
+// Workspace of oc_attn_forward_v_repair_noalloc: a file-scope device array,
+// one copy per GPU, held until the process ends. Host code never passes the
+// array's name to a kernel (on the host it only stands for the symbol):
+// it looks up each device's own address once, with that device current,
+// and passes that.
+static __device__ __align__(256) uint8_t scratch[OC_NOALLOC_WORKSPACE_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// device address of the current device's scratch array (looked up on the
+// first call on each device)
+oc_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= MAX_DEVICES) return OC_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (!ptr) return hip_fail(hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return OC_OK;
+}
+}  // namespace
+
 extern "C" {
 
 oc_status oc_attn_plan_create(const oc_attn_desc* desc, double max_repair_budget, oc_attn_plan** plan) {
@@ -419,6 +452,30 @@ oc_status oc_attn_forward_v_repair(oc_attn_plan* p, const void* q, const void* k
   const int n_sel = repair_count(budget, p->d.S);
   s = run_prepare(p, q, k, v, ws, n_sel, (hipStream_t)stream);
   if (s != OC_OK) return s;
+  return run_attention(p, ws, out, n_sel, (hipStream_t)stream);
+}
+
+oc_status oc_attn_forward_v_repair_noalloc(oc_attn_plan* p, const void* q, const void* k, const void* v,
+                                          double budget, void* out, void* stream) {
+  if (!p) return OC_ERR_INVALID_ARGUMENT;
+  if (p->L.total_bytes > OC_NOALLOC_WORKSPACE_BYTES) return OC_ERR_WORKSPACE_TOO_SMALL;
+  oc_status s = check_budget(p, budget);
+  if (s != OC_OK) return s;
+  void* ws = nullptr;
+  s = scratch_address(&ws);
+  if (s != OC_OK) return s;
+  const size_t ws_bytes = OC_NOALLOC_WORKSPACE_BYTES;
+  s = check_inputs(p, q, k, v, ws, ws_bytes);
+  if (s != OC_OK) return s;
+  const void* ins[3] = {q, k, v};
+  s = check_out(p, out, ins, 3, ws, ws_bytes);
+  if (s != OC_OK) return s;
+  // the kernels one by one: no graph is captured or instantiated here
+  const int n_sel = repair_count(budget, p->d.S);
+  const hipError_t e = launch_prepare(prep_args(p, q, k, v, ws, n_sel > 0 ? n_sel : -1), p->d.dtype == OC_FP16,
+                                      (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e);
+  p->mark_prepared(ws, n_sel > 0 ? n_sel : -1, p->v_smooth);
   return run_attention(p, ws, out, n_sel, (hipStream_t)stream);
 }
 

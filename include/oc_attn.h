@@ -210,6 +210,30 @@ oc_status oc_attn_prepare_v_repair(oc_attn_plan* plan, const void* q, const void
 oc_status oc_attn_forward_v_repair(oc_attn_plan* plan, const void* q, const void* k, const void* v,
                                    double budget, void* out, void* ws, size_t ws_bytes, void* stream);
 
+/* Capacity of the workspace inside the library used by
+ * oc_attn_forward_v_repair_noalloc (per GPU): 64 MiB, enough for a plan such
+ * as B=1, S=8192, H=8 with repair (oc_attn_workspace_size tells). */
+#define OC_NOALLOC_WORKSPACE_BYTES (64ull << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * computation and result as oc_attn_forward_v_repair (budget 0: as
+ * oc_attn_forward), with the workspace taken from a device array inside the
+ * library instead of a caller's buffer. The call allocates nothing and
+ * captures no graph: it enqueues the prepare and attention kernels directly
+ * on `stream`. The array holds OC_NOALLOC_WORKSPACE_BYTES per GPU, for the
+ * life of the process; a plan whose oc_attn_workspace_size exceeds that gives
+ * OC_ERR_WORKSPACE_TOO_SMALL. Every call on one GPU uses that GPU's one
+ * array, so calls that overlap in time on one GPU (concurrent streams, or
+ * threads) race and must be serialized by the caller; consecutive calls on
+ * one stream are ordered and safe. Nothing in the array needs to start at
+ * zero: the prepare step writes every byte the attention reads. The first
+ * call on a device, with that device current, looks up the array's address
+ * there; a failing lookup gives OC_ERR_HIP. Validation as
+ * oc_attn_forward_v_repair. */
+oc_status oc_attn_forward_v_repair_noalloc(oc_attn_plan* plan, const void* q, const void* k, const void* v,
+                                          double budget, void* out, void* stream);
+
 /* Attention only, on a workspace this plan prepared earlier (kernel-alone
  * timing; the plan remembers its 64 most recently prepared workspaces).
  * with_repair != 0 requires the workspace to come from

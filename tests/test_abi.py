@@ -216,3 +216,29 @@ def test_set_v_smoothing_accepts_0_and_1():
         assert L.total_bytes >= L.vmu + 4 * nT * 128 * 2
     finally:
         lib.oc_attn_plan_destroy(p)
+
+
+def test_noalloc_entry_rejects_before_any_hip_call():
+    """The allocation-free call checks the plan's workspace size against the
+    library's array and the budget before it touches the GPU."""
+    big = make_desc(B=1, S=73397, H=56)
+    st, p = create(big)
+    assert st == oc.OC_OK
+    try:
+        n = ctypes.c_size_t()
+        lib.oc_attn_workspace_size(p, ctypes.byref(n))
+        assert n.value > oc.NOALLOC_WORKSPACE_BYTES
+        assert lib.oc_attn_forward_v_repair_noalloc(p, vp(FAKE), vp(FAKE + (1 << 33)), vp(FAKE + (1 << 34)),
+                                                    ctypes.c_double(0.0), vp(FAKE + (1 << 35)), None) == \
+            oc.OC_ERR_WORKSPACE_TOO_SMALL
+    finally:
+        lib.oc_attn_plan_destroy(p)
+    st, p = create(make_desc(S=1000, H=2), 0.01)
+    try:
+        for b in (-0.1, 0.5, math.nan):          # 0.5 exceeds the plan's 0.01
+            assert lib.oc_attn_forward_v_repair_noalloc(p, vp(FAKE), vp(FAKE), vp(FAKE), ctypes.c_double(b),
+                                                        vp(FAKE), None) == oc.OC_ERR_INVALID_ARGUMENT
+        assert lib.oc_attn_forward_v_repair_noalloc(None, vp(FAKE), vp(FAKE), vp(FAKE), ctypes.c_double(0.0),
+                                                    vp(FAKE), None) == oc.OC_ERR_INVALID_ARGUMENT
+    finally:
+        lib.oc_attn_plan_destroy(p)
