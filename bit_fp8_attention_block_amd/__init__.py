@@ -26,7 +26,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboc_attn.so")
+# the in-tree build; OC_ATTN_LIB names another build of the same library
+# (the sanitizer build the boundary tests run against)
+LIB_PATH = os.environ.get("OC_ATTN_LIB") or os.path.join(_HERE, "liboc_attn.so")
 
 OC_OK, OC_ERR_INVALID_ARGUMENT, OC_ERR_UNSUPPORTED, OC_ERR_WORKSPACE_TOO_SMALL, OC_ERR_NOT_PREPARED, OC_ERR_HIP = range(6)
 OC_BF16, OC_FP16 = 0, 1
