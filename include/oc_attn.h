@@ -190,23 +190,44 @@ oc_status oc_attn_workspace_size(const oc_attn_plan* plan, size_t* bytes);
 oc_status oc_attn_workspace_layout(const oc_attn_plan* plan, oc_attn_ws_layout* layout);
 
 /* Quantize q, k, v into the workspace: per-block Q/K scales and E4M3 codes,
- * per-head V scale and codes packed transposed for the matrix cores. The
- * prepare kernels run as one captured hipGraph. */
+ * per-head V scale and codes packed transposed for the matrix cores (Open VC
+ * Attention product page, kernel paragraph: per-block Q/K and per-head V
+ * scales; the call quantizes to FP8 itself, API paragraph). The prepare
+ * kernels run as one captured hipGraph (Open-VC news, "Архитектурные
+ * оптимизации": Q/K/V preparation fused into one graph).
+ * q, k, v: device, [B,S,H,128] bf16/fp16 with the plan's strides; ws: device,
+ * at least oc_attn_workspace_size bytes, 256-byte aligned, overwritten;
+ * stream: hipStream_t. Errors as listed at the top of this file. */
 oc_status oc_attn_prepare(oc_attn_plan* plan, const void* q, const void* k, const void* v,
                           void* ws, size_t ws_bytes, void* stream);
 
-/* Full call: oc_attn_prepare, then ExpCast attention into out (BF16). */
+/* Full call: oc_attn_prepare, then ExpCast attention into out (BF16,
+ * contiguous [B,S,H,128], device, caller-owned). Softmax weights are E4M3
+ * bytes from one FMA on the log-domain score against the bit-aligned
+ * running row max, keys visited from the middle of the window (VC-Attention
+ * write-up, "ExpCast-FP8"; product page, kernel paragraph); non-causal
+ * attention with head dim 128 on bf16/fp16 inputs, BF16 output (product page,
+ * API paragraph). Errors as listed at the top of this file. */
 oc_status oc_attn_forward(oc_attn_plan* plan, const void* q, const void* k, const void* v,
                           void* out, void* ws, size_t ws_bytes, void* stream);
 
 /* oc_attn_prepare plus the repair set for `budget` (0 <= budget <= the plan's
- * max): residual energy of every value token, the top ceil(budget*S) tokens
- * per (b, h) (ties to the lower index), and their E4M3 residuals. */
+ * max): residual energy of every value token (sum of squares of
+ * v - sv*dec(v_hat) over the channels, float64, added pairwise in channel
+ * order), the top ceil(budget*S) tokens per (b, h) (ties to the lower
+ * index), and their E4M3 residuals with their own per-head scale (Open-VC
+ * news, "Решение: ExpCast и отказ от экспонент": repair of the worst-rounded
+ * value tokens; product page, repair paragraph: prepare with a budget such
+ * as 0.005). A budget outside [0, plan max] or NaN gives
+ * OC_ERR_INVALID_ARGUMENT; other errors as oc_attn_prepare. */
 oc_status oc_attn_prepare_v_repair(oc_attn_plan* plan, const void* q, const void* k, const void* v,
                                    double budget, void* ws, size_t ws_bytes, void* stream);
 
 /* Full call with repair: oc_attn_prepare_v_repair, then attention whose
- * output adds the repaired residuals with the unrepaired row sums. */
+ * output adds the repaired residuals with the unrepaired row sums (product
+ * page, repair paragraph: the repaired attention call after
+ * prepare_v_repair). Arguments and errors as oc_attn_forward plus the budget
+ * rule of oc_attn_prepare_v_repair. */
 oc_status oc_attn_forward_v_repair(oc_attn_plan* plan, const void* q, const void* k, const void* v,
                                    double budget, void* out, void* ws, size_t ws_bytes, void* stream);
 
