@@ -41,7 +41,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 # rocprofv3 PMC counters (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors a
 # plain 4 GiB copy gives; profiles/attn_kernel_s73397_h56.md). They are only
 # reported while the kernel sources still hash to the measured version.
-MEASURED_TRAFFIC = {"sources_sha256": "65406fbd42fbb56fa640e9c28f8a002fd361e21b8e7baad8e25b2c602685fdd0", "bytes": 11962702795}
+MEASURED_TRAFFIC = {"sources_sha256": "fdbec5f384ab038b8934e004a77e41a052473fc3b25fd97c6bac6f107ca569b1", "bytes": 11962793867}
 KERNEL_SOURCES = ("bit_fp8_attention_block_amd/csrc/attention.hip", "bit_fp8_attention_block_amd/csrc/oc_common.h")
 
 
@@ -166,6 +166,9 @@ def main():
     ap.add_argument("--weights", default="expcast", choices=("expcast", "exp_fp8"),
                     help="byte path of the kernel timed by --kernel-only")
     ap.add_argument("--prepare-only", action="store_true", help="time only the prepare step (for profiling)")
+    ap.add_argument("--tile-scan", action="store_true",
+                    help="kernel-alone time on random inputs at grids of 256 workgroups with 8..256 key tiles, "
+                         "and on a few grids smaller than the chip (fixed cost per launch vs cost per tile)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -177,6 +180,27 @@ def main():
         ms, _ = timed_calls(lambda: dst.copy_(src), 3, 1)
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copy_ms": ms,
                           "copy_gbs": 2 * n / ms / 1e6}))
+        return
+
+    if args.tile_scan:
+        import bit_fp8_attention_block_amd as oc
+        g = torch.Generator(device="cuda").manual_seed(1)
+        rows = []
+        for S, H in ((1024, 64), (2048, 32), (4096, 16), (8192, 8), (16384, 4), (32768, 2),
+                     (1024, 2), (2048, 2), (4096, 1), (8192, 1)):
+            q, k, v = (torch.randn(1, S, H, 128, device="cuda", generator=g).to(torch.bfloat16) for _ in range(3))
+            prep = oc.prepare(q, k, v)
+            out = torch.empty_like(q)
+            times = [timed_calls(lambda: oc.attention_prepared(prep, out=out), 1, 0)[0] for _ in range(30)]
+            t = float(np.median(times))
+            rec = {"S": S, "H": H, "key_tiles": -(-S // 128), "workgroups": H * -(-S // 256), "kernel_us": round(1e3 * t, 1),
+                   "tflops": round(oc.flops(1, S, H) / t / 1e9, 1)}
+            log(json.dumps(rec))
+            rows.append(rec)
+            del prep
+        full = [r for r in rows if r["workgroups"] == 256]
+        slope, icpt = np.polyfit([r["key_tiles"] for r in full], [r["kernel_us"] for r in full], 1)
+        print(json.dumps({"tile_scan": rows, "us_per_tile": round(float(slope), 3), "us_per_launch": round(float(icpt), 1)}))
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
