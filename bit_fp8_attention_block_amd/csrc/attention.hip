@@ -88,28 +88,43 @@ __device__ inline int tile_at(int s, int c, int nT, int order) {
   return left > right ? c - m - extra : c + m + extra;
 }
 
-// One 16 KiB tile from global memory into LDS by direct global->LDS loads:
-// 1024 chunks of 16 bytes; each instruction moves 1 KiB per wave, lane l's
-// chunk landing at wave base + 16*l (the base is taken from M0). Threads
-// 0..NT-1 take part; chunk i*NT + t of the tile is thread t's i-th.
-// The global address is a scalar base (tile + i*NT*16) plus the per-lane
-// offset voff = 16*t, and the LDS address is a scalar offset, so issuing a
-// tile costs no vector instructions.
+// One 16 KiB tile from global memory into LDS by direct global->LDS loads,
+// the LDS copy laid out as the tile is in memory. Threads 0..NT-1 take part:
+// wave wv copies the contiguous 16384*64/NT bytes at wv*16384*64/NT, one KiB
+// per instruction, lane l's 16 bytes landing at the wave's LDS base + 16*l.
+// The base comes from M0 and the instruction's immediate offset (i KiB) is
+// added to both the global and the LDS address, so a wave sets M0 once per
+// tile and the loads differ only in that immediate; the global address is a
+// scalar base plus the per-lane offset lane16 = 16*lane. Issuing a tile
+// costs no vector instructions.
 // Written as inline assembly so that the compiler does not track these loads:
 // it would otherwise drain all of them (vmcnt(0)) before every LDS read and
 // at every barrier, which rules out keeping a tile load in flight across an
 // iteration. The caller orders them with explicit vmcnt waits and
 // lds_barrier(). The s_nop covers the M0-write -> LDS-DMA hazard.
 template <int NT>
-__device__ inline void load_tile(uint32_t lds_dst, const uint8_t* src, uint32_t voff, int wv) {
-#pragma unroll
-  for (int i = 0; i < 1024 / NT; ++i) {
-    const uint32_t m0 = lds_dst + (uint32_t)(i * NT + wv * 64) * 16u;
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+__device__ inline void load_tile(uint32_t lds_dst, const uint8_t* src, uint32_t lane16, int wv) {
+  constexpr int PER = 1024 / NT;   // instructions (KiB) per wave
+  static_assert(PER == 2 || PER == 4, "a tile is split over 4 or 8 waves");
+  const uint32_t base = (uint32_t)wv * (PER * 1024u);
+  const uint32_t m0 = lds_dst + base;
+  const uint8_t* g = src + base;
+  if constexpr (PER == 2)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, %2\n\t"
+                 "global_load_lds_dwordx4 %1, %2 offset:1024"
                  :
-                 : "s"(m0), "v"(voff), "s"(src + i * NT * 16)
+                 : "s"(m0), "v"(lane16), "s"(g)
                  : "memory", "m0");
-  }
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, %2\n\t"
+                 "global_load_lds_dwordx4 %1, %2 offset:1024\n\t"
+                 "global_load_lds_dwordx4 %1, %2 offset:2048\n\t"
+                 "global_load_lds_dwordx4 %1, %2 offset:3072"
+                 :
+                 : "s"(m0), "v"(lane16), "s"(g)
+                 : "memory", "m0");
 }
 
 // byte offset in the workgroup's LDS of a pointer into it
@@ -608,7 +623,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   // LDS offsets of the K, V and block-mean buffers, and the per-lane offsets
   // of the direct loads
   const uint32_t kofs = lds_offset(kbuf), vofs = lds_offset(vbuf), mofs = lds_offset(mubuf);
-  const uint32_t voff = 16u * tid, voff_mu = 4u * lane;
+  const uint32_t voff = 16u * lane, voff_mu = 4u * lane;
   const int q0 = qt * BQ + wv * QBW * 16;
   const int qrow0 = q0 + l16;
   const int nT = a.nT;
@@ -673,9 +688,10 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
     if (i < nT) load_tile<NTHREADS>(vofs + i * TILE_BYTES, vt_ptr(i), voff, wvs);
-  const auto mu_ptr = [&](int step) {
-    return reinterpret_cast<const uint8_t*>(a.vmu + ((int64_t)bh * nT + tile_at(step, centre, nT, a.order)) * HEAD_DIM);
+  const auto mu_of = [&](int tile) {
+    return reinterpret_cast<const uint8_t*>(a.vmu + ((int64_t)bh * nT + tile) * HEAD_DIM);
   };
+  const auto mu_ptr = [&](int step) { return mu_of(tile_at(step, centre, nT, a.order)); };
   const float vinv = VSMOOTH ? a.sv[2 * bh + 1] : 0.0f;
   if (VSMOOTH) {
     // slots of steps never loaded are read by the last flush of a short
@@ -698,15 +714,21 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   // PV. Group B reads both before the barrier that ends an iteration.
   v8i pre[KPRE > RA ? KPRE : RA];
   v8i bpre[RA];
+  // group A carries the key tiles of steps s, s+1 and s+2 (the ExpCast's
+  // scale, the V load) from one iteration to the next and works out only
+  // that of step s+3 (the K load)
+  int ta0 = tile_at(0, centre, nT, a.order), ta1 = tile_at(1, centre, nT, a.order);
+  int ta2 = tile_at(2, centre, nT, a.order);
 
   // One iteration of the tile loop. Before the last three steps (TAIL
   // false) every tile load is issued, so the load flags are constants.
   const auto iteration = [&](int s, auto tail, auto grp) {
     constexpr bool TAIL = decltype(tail)::value;
     constexpr bool GB = decltype(grp)::value;   // group B
-    const int j = tile_at(s, centre, nT, a.order);
+    const int j = GB ? tile_at(s, centre, nT, a.order) : ta0;
     const int b0 = s & (NBUF - 1), b1 = (s + 1) & (NBUF - 1), bm1 = (s - 1) & (NBUF - 1);
     const bool ld_k = !TAIL || s + 3 < nT, ld_v = !TAIL || s + 2 < nT;
+    const int t3 = (ld_k && !GB) ? tile_at(s + 3, centre, nT, a.order) : 0;
     if (!GB) {
       // V tile s is in LDS since the last barrier: its first operands arrive
       // while the ExpCast below runs, so the PV MFMAs start without waiting
@@ -714,11 +736,11 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
       for (int i = 0; i < RA; ++i) pre[i] = lds_operand(vbuf + b0 * TILE_BYTES, i, lane);
     }
     // (group A is waves 0-3, threads 0-255)
-    if (ld_k && !GB) load_tile<NTHREADS / 2>(kofs + ((s + 3) & (NBUF - 1)) * TILE_BYTES, kt_ptr(s + 3), voff, wvs);
-    if (ld_v && !GB) load_tile<NTHREADS / 2>(vofs + ((s + 2) & (NBUF - 1)) * TILE_BYTES, vt_ptr(s + 2), voff, wvs);
+    if (ld_k && !GB) load_tile<NTHREADS / 2>(kofs + ((s + 3) & (NBUF - 1)) * TILE_BYTES, kg + (int64_t)t3 * TILE_BYTES, voff, wvs);
+    if (ld_v && !GB) load_tile<NTHREADS / 2>(vofs + ((s + 2) & (NBUF - 1)) * TILE_BYTES, vg + (int64_t)ta2 * TILE_BYTES, voff, wvs);
     // V-Smooth: one more 1 KiB load on wave 0, the block means of tile s+2
     const bool ld_mu = VSMOOTH && ld_v && wv == 0;
-    if (ld_mu) load_means(mofs + ((s + 2) & (MU_NBUF - 1)) * MU_SLOT, mu_ptr(s + 2), voff_mu);
+    if (ld_mu) load_means(mofs + ((s + 2) & (MU_NBUF - 1)) * MU_SLOT, mu_of(ta2), voff_mu);
     const float skj = skp[j];
     if (!GB) {
       expcast_tile<DUMP, EXPP>(S, P, aq8, skj, Mv, Mr, sb, O, L, C, j, j == last_masked, a, g, dslot);
@@ -730,6 +752,9 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
         ofence(O);
       }
       if (s + 1 < nT) qk_tile(kbuf + b1 * TILE_BYTES, qop, S, lane);
+      ta0 = ta1;
+      ta1 = ta2;
+      ta2 = t3;
     } else {
       __builtin_amdgcn_s_setprio(2);
       qk_tile<KPRE>(kbuf + b0 * TILE_BYTES, qop, S, lane, pre);
