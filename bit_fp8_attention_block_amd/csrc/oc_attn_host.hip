@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -340,11 +341,43 @@ oc_status scratch_address(void** out) {
   *out = g_scratch_ptr[dev];
   return OC_OK;
 }
+// One line per C-ABI call on stderr when the environment sets OC_ATTN_LOG=1
+// (read once): the entry point, the plan's shape and options, the budget of
+// the repair calls, and the status (with the HIP error for OC_ERR_HIP).
+bool log_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("OC_ATTN_LOG");
+    return e != nullptr && std::atoi(e) == 1;
+  }();
+  return on;
+}
+
+oc_status logged(const char* fn, const oc_attn_plan* p, oc_status s, double budget,
+                 const oc_attn_desc* desc = nullptr) {
+  if (!log_enabled()) return s;
+  char line[512];
+  int n = std::snprintf(line, sizeof line, "[oc_attn] %s", fn);
+  const oc_attn_desc* d = p ? &p->d : desc;
+  if (d && n > 0 && n < (int)sizeof line)
+    n += std::snprintf(line + n, sizeof line - n, " B=%d S=%d H=%d D=%d %s", d->B, d->S, d->H, d->D,
+                       d->dtype == OC_FP16 ? "fp16" : "bf16");
+  if (p && n > 0 && n < (int)sizeof line)
+    n += std::snprintf(line + n, sizeof line - n, " weights=%s v_smooth=%d k_smooth=%d",
+                       p->exp_path ? "exp_fp8" : "expcast", p->v_smooth, p->k_smooth);
+  if (budget >= 0.0 && n > 0 && n < (int)sizeof line)
+    n += std::snprintf(line + n, sizeof line - n, " budget=%g", budget);
+  if (n > 0 && n < (int)sizeof line)
+    n += std::snprintf(line + n, sizeof line - n, " -> %s", oc_attn_status_string(s));
+  if (s == OC_ERR_HIP && n > 0 && n < (int)sizeof line)
+    n += std::snprintf(line + n, sizeof line - n, " (%s)", hipGetErrorString((hipError_t)g_last_hip_error));
+  std::fprintf(stderr, "%s\n", line);
+  return s;
+}
 }  // namespace
 
 extern "C" {
 
-oc_status oc_attn_plan_create(const oc_attn_desc* desc, double max_repair_budget, oc_attn_plan** plan) {
+static oc_status plan_create_impl(const oc_attn_desc* desc, double max_repair_budget, oc_attn_plan** plan) {
   if (!desc || !plan) return OC_ERR_INVALID_ARGUMENT;
   *plan = nullptr;
   const oc_attn_desc& d = *desc;
@@ -371,19 +404,19 @@ oc_status oc_attn_plan_create(const oc_attn_desc* desc, double max_repair_budget
   return OC_OK;
 }
 
-oc_status oc_attn_plan_set_weights(oc_attn_plan* p, int weights) {
+static oc_status plan_set_weights_impl(oc_attn_plan* p, int weights) {
   if (!p || (weights != OC_WEIGHTS_EXPCAST && weights != OC_WEIGHTS_EXP_FP8)) return OC_ERR_INVALID_ARGUMENT;
   p->exp_path = weights == OC_WEIGHTS_EXP_FP8 ? 1 : 0;
   return OC_OK;
 }
 
-oc_status oc_attn_plan_set_v_smoothing(oc_attn_plan* p, int enable) {
+static oc_status plan_set_v_smoothing_impl(oc_attn_plan* p, int enable) {
   if (!p || (enable != 0 && enable != 1)) return OC_ERR_INVALID_ARGUMENT;
   p->v_smooth = enable;
   return OC_OK;
 }
 
-oc_status oc_attn_plan_set_k_smoothing(oc_attn_plan* p, int enable) {
+static oc_status plan_set_k_smoothing_impl(oc_attn_plan* p, int enable) {
   if (!p || (enable != 0 && enable != 1)) return OC_ERR_INVALID_ARGUMENT;
   p->k_smooth = enable;
   return OC_OK;
@@ -396,19 +429,19 @@ void oc_attn_plan_destroy(oc_attn_plan* p) {
   delete p;
 }
 
-oc_status oc_attn_workspace_size(const oc_attn_plan* p, size_t* bytes) {
+static oc_status workspace_size_impl(const oc_attn_plan* p, size_t* bytes) {
   if (!p || !bytes) return OC_ERR_INVALID_ARGUMENT;
   *bytes = (size_t)p->L.total_bytes;
   return OC_OK;
 }
 
-oc_status oc_attn_workspace_layout(const oc_attn_plan* p, oc_attn_ws_layout* layout) {
+static oc_status workspace_layout_impl(const oc_attn_plan* p, oc_attn_ws_layout* layout) {
   if (!p || !layout) return OC_ERR_INVALID_ARGUMENT;
   *layout = p->L;
   return OC_OK;
 }
 
-oc_status oc_attn_prepare(oc_attn_plan* p, const void* q, const void* k, const void* v, void* ws, size_t ws_bytes,
+static oc_status prepare_impl(oc_attn_plan* p, const void* q, const void* k, const void* v, void* ws, size_t ws_bytes,
                           void* stream) {
   if (!p) return OC_ERR_INVALID_ARGUMENT;
   oc_status s = check_inputs(p, q, k, v, ws, ws_bytes);
@@ -416,7 +449,7 @@ oc_status oc_attn_prepare(oc_attn_plan* p, const void* q, const void* k, const v
   return run_prepare(p, q, k, v, ws, -1, (hipStream_t)stream);
 }
 
-oc_status oc_attn_forward(oc_attn_plan* p, const void* q, const void* k, const void* v, void* out, void* ws,
+static oc_status forward_impl(oc_attn_plan* p, const void* q, const void* k, const void* v, void* out, void* ws,
                           size_t ws_bytes, void* stream) {
   if (!p) return OC_ERR_INVALID_ARGUMENT;
   oc_status s = check_inputs(p, q, k, v, ws, ws_bytes);
@@ -429,7 +462,7 @@ oc_status oc_attn_forward(oc_attn_plan* p, const void* q, const void* k, const v
   return run_attention(p, ws, out, 0, (hipStream_t)stream);
 }
 
-oc_status oc_attn_prepare_v_repair(oc_attn_plan* p, const void* q, const void* k, const void* v, double budget,
+static oc_status prepare_v_repair_impl(oc_attn_plan* p, const void* q, const void* k, const void* v, double budget,
                                    void* ws, size_t ws_bytes, void* stream) {
   if (!p) return OC_ERR_INVALID_ARGUMENT;
   oc_status s = check_budget(p, budget);
@@ -439,7 +472,7 @@ oc_status oc_attn_prepare_v_repair(oc_attn_plan* p, const void* q, const void* k
   return run_prepare(p, q, k, v, ws, repair_count(budget, p->d.S), (hipStream_t)stream);
 }
 
-oc_status oc_attn_forward_v_repair(oc_attn_plan* p, const void* q, const void* k, const void* v, double budget,
+static oc_status forward_v_repair_impl(oc_attn_plan* p, const void* q, const void* k, const void* v, double budget,
                                    void* out, void* ws, size_t ws_bytes, void* stream) {
   if (!p) return OC_ERR_INVALID_ARGUMENT;
   oc_status s = check_budget(p, budget);
@@ -455,7 +488,7 @@ oc_status oc_attn_forward_v_repair(oc_attn_plan* p, const void* q, const void* k
   return run_attention(p, ws, out, n_sel, (hipStream_t)stream);
 }
 
-oc_status oc_attn_forward_v_repair_noalloc(oc_attn_plan* p, const void* q, const void* k, const void* v,
+static oc_status forward_v_repair_noalloc_impl(oc_attn_plan* p, const void* q, const void* k, const void* v,
                                           double budget, void* out, void* stream) {
   if (!p) return OC_ERR_INVALID_ARGUMENT;
   if (p->L.total_bytes > OC_NOALLOC_WORKSPACE_BYTES) return OC_ERR_WORKSPACE_TOO_SMALL;
@@ -479,7 +512,7 @@ oc_status oc_attn_forward_v_repair_noalloc(oc_attn_plan* p, const void* q, const
   return run_attention(p, ws, out, n_sel, (hipStream_t)stream);
 }
 
-oc_status oc_attn_forward_prepared(oc_attn_plan* p, const void* ws, size_t ws_bytes, void* out, int with_repair,
+static oc_status forward_prepared_impl(oc_attn_plan* p, const void* ws, size_t ws_bytes, void* out, int with_repair,
                                    void* stream) {
   if (!p || !ws || ((uintptr_t)ws & 255u)) return OC_ERR_INVALID_ARGUMENT;
   if (ws_bytes < p->L.total_bytes) return OC_ERR_WORKSPACE_TOO_SMALL;
@@ -491,7 +524,7 @@ oc_status oc_attn_forward_prepared(oc_attn_plan* p, const void* ws, size_t ws_by
   return run_attention(p, ws, out, with_repair ? state : 0, (hipStream_t)stream);
 }
 
-oc_status oc_attn_debug_pcodes(oc_attn_plan* p, const void* ws, size_t ws_bytes, int32_t b, int32_t h,
+static oc_status debug_pcodes_impl(oc_attn_plan* p, const void* ws, size_t ws_bytes, int32_t b, int32_t h,
                                const int32_t* rows, int32_t n_rows, int32_t with_repair, uint8_t* codes,
                                int32_t* m_used, float* scores, uint8_t* rcodes, float* out_f32, void* out,
                                void* stream) {
@@ -534,5 +567,68 @@ const char* oc_attn_status_string(oc_status s) {
 }
 
 int oc_attn_last_hip_error(void) { return g_last_hip_error; }
+
+
+oc_status oc_attn_plan_create(const oc_attn_desc* desc, double max_repair_budget, oc_attn_plan** plan) {
+  const oc_status s = plan_create_impl(desc, max_repair_budget, plan);
+  return logged("oc_attn_plan_create", s == OC_OK ? *plan : nullptr, s, max_repair_budget, desc);
+}
+
+oc_status oc_attn_plan_set_weights(oc_attn_plan* p, int weights) {
+  return logged("oc_attn_plan_set_weights", p, plan_set_weights_impl(p, weights), -1.0);
+}
+
+oc_status oc_attn_plan_set_v_smoothing(oc_attn_plan* p, int enable) {
+  return logged("oc_attn_plan_set_v_smoothing", p, plan_set_v_smoothing_impl(p, enable), -1.0);
+}
+
+oc_status oc_attn_plan_set_k_smoothing(oc_attn_plan* p, int enable) {
+  return logged("oc_attn_plan_set_k_smoothing", p, plan_set_k_smoothing_impl(p, enable), -1.0);
+}
+
+oc_status oc_attn_workspace_size(const oc_attn_plan* p, size_t* bytes) {
+  return logged("oc_attn_workspace_size", p, workspace_size_impl(p, bytes), -1.0);
+}
+
+oc_status oc_attn_workspace_layout(const oc_attn_plan* p, oc_attn_ws_layout* layout) {
+  return logged("oc_attn_workspace_layout", p, workspace_layout_impl(p, layout), -1.0);
+}
+
+oc_status oc_attn_prepare(oc_attn_plan* p, const void* q, const void* k, const void* v, void* ws, size_t ws_bytes,
+                          void* stream) {
+  return logged("oc_attn_prepare", p, prepare_impl(p, q, k, v, ws, ws_bytes, stream), -1.0);
+}
+
+oc_status oc_attn_forward(oc_attn_plan* p, const void* q, const void* k, const void* v, void* out, void* ws,
+                          size_t ws_bytes, void* stream) {
+  return logged("oc_attn_forward", p, forward_impl(p, q, k, v, out, ws, ws_bytes, stream), -1.0);
+}
+
+oc_status oc_attn_prepare_v_repair(oc_attn_plan* p, const void* q, const void* k, const void* v, double budget,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  return logged("oc_attn_prepare_v_repair", p, prepare_v_repair_impl(p, q, k, v, budget, ws, ws_bytes, stream), budget);
+}
+
+oc_status oc_attn_forward_v_repair(oc_attn_plan* p, const void* q, const void* k, const void* v, double budget,
+                                   void* out, void* ws, size_t ws_bytes, void* stream) {
+  return logged("oc_attn_forward_v_repair", p, forward_v_repair_impl(p, q, k, v, budget, out, ws, ws_bytes, stream), budget);
+}
+
+oc_status oc_attn_forward_v_repair_noalloc(oc_attn_plan* p, const void* q, const void* k, const void* v,
+                                          double budget, void* out, void* stream) {
+  return logged("oc_attn_forward_v_repair_noalloc", p, forward_v_repair_noalloc_impl(p, q, k, v, budget, out, stream), budget);
+}
+
+oc_status oc_attn_forward_prepared(oc_attn_plan* p, const void* ws, size_t ws_bytes, void* out, int with_repair,
+                                   void* stream) {
+  return logged("oc_attn_forward_prepared", p, forward_prepared_impl(p, ws, ws_bytes, out, with_repair, stream), -1.0);
+}
+
+oc_status oc_attn_debug_pcodes(oc_attn_plan* p, const void* ws, size_t ws_bytes, int32_t b, int32_t h,
+                               const int32_t* rows, int32_t n_rows, int32_t with_repair, uint8_t* codes,
+                               int32_t* m_used, float* scores, uint8_t* rcodes, float* out_f32, void* out,
+                               void* stream) {
+  return logged("oc_attn_debug_pcodes", p, debug_pcodes_impl(p, ws, ws_bytes, b, h, rows, n_rows, with_repair, codes, m_used, scores, rcodes, out_f32, out, stream), -1.0);
+}
 
 }  // extern "C"

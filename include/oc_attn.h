@@ -66,6 +66,12 @@
  *     (or, with repair, not prepared with repair) gives OC_ERR_NOT_PREPARED.
  *   A failing HIP call gives OC_ERR_HIP. oc_attn_last_hip_error() then
  *   returns the hipError_t of the calling thread's last failure.
+ *
+ * Logging: with OC_ATTN_LOG=1 in the environment (read once per process),
+ * every call above writes one line to stderr: the entry point, the plan's
+ * B, S, H, D, dtype and options, the budget of the repair calls, and the
+ * status (with the HIP error's text for OC_ERR_HIP). Otherwise the library
+ * prints nothing.
  * NaN or Inf inputs are not supported; the output for them is undefined.
  * Otherwise the output is finite wherever the method's own result is, with
  * one exception in the V-Smooth option (oc_attn_plan_set_v_smoothing): when

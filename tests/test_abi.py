@@ -242,3 +242,51 @@ def test_noalloc_entry_rejects_before_any_hip_call():
                                                     vp(FAKE), None) == oc.OC_ERR_INVALID_ARGUMENT
     finally:
         lib.oc_attn_plan_destroy(p)
+
+
+_LOG_CHILD = r"""
+import ctypes, sys
+import bit_fp8_attention_block_amd as oc
+lib = oc._lib
+d = oc.Desc(1, 1000, 4, 128, oc.OC_BF16, 1000 * 4 * 128, 4 * 128, 128, 0.0)
+p = ctypes.c_void_p()
+assert lib.oc_attn_plan_create(ctypes.byref(d), ctypes.c_double(0.01), ctypes.byref(p)) == oc.OC_OK
+n = ctypes.c_size_t()
+assert lib.oc_attn_workspace_size(p, ctypes.byref(n)) == oc.OC_OK
+assert lib.oc_attn_plan_set_weights(p, 9) == oc.OC_ERR_INVALID_ARGUMENT
+assert lib.oc_attn_forward_v_repair(p, None, None, None, ctypes.c_double(0.5), None, None, n.value,
+                                    None) == oc.OC_ERR_INVALID_ARGUMENT
+bad = oc.Desc(1, 1000, 4, 64, oc.OC_BF16, 1000 * 4 * 128, 4 * 128, 128, 0.0)
+q = ctypes.c_void_p()
+assert lib.oc_attn_plan_create(ctypes.byref(bad), ctypes.c_double(0.0), ctypes.byref(q)) == oc.OC_ERR_UNSUPPORTED
+lib.oc_attn_plan_destroy(p)
+print("child done")
+"""
+
+
+@pytest.mark.parametrize("on", [True, False])
+def test_call_log_on_stderr_only_when_asked(on):
+    """With OC_ATTN_LOG=1 every C-ABI call writes one line to stderr (entry
+    point, shape, options, budget, status); without it, nothing."""
+    import subprocess
+    import sys
+    env = dict(os.environ)
+    env.pop("OC_ATTN_LOG", None)
+    if on:
+        env["OC_ATTN_LOG"] = "1"
+    env["PYTHONPATH"] = ROOT + os.pathsep + env.get("PYTHONPATH", "")
+    r = subprocess.run([sys.executable, "-c", _LOG_CHILD], env=env, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert "child done" in r.stdout
+    lines = [l for l in r.stderr.splitlines() if l.startswith("[oc_attn]")]
+    if not on:
+        assert lines == []
+        return
+    assert len(lines) == 5, lines
+    assert lines[0] == "[oc_attn] oc_attn_plan_create B=1 S=1000 H=4 D=128 bf16 weights=expcast v_smooth=0 " \
+                       "k_smooth=0 budget=0.01 -> ok"
+    assert lines[1].startswith("[oc_attn] oc_attn_workspace_size B=1 S=1000") and lines[1].endswith("-> ok")
+    assert lines[2].startswith("[oc_attn] oc_attn_plan_set_weights") and lines[2].endswith("-> invalid argument")
+    assert "budget=0.5" in lines[3] and lines[3].endswith("-> invalid argument")
+    assert lines[4] == "[oc_attn] oc_attn_plan_create B=1 S=1000 H=4 D=64 bf16 budget=0 -> " \
+                       "unsupported (D must be 128; dtype bf16 or fp16)"
