@@ -171,7 +171,24 @@ def main():
                          "and on a few grids smaller than the chip (fixed cost per launch vs cost per tile)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference for the HBM byte counters)")
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="only time the vendor library's FP8 GEMM (torch._scaled_mm, E4M3 in, bf16 out) at large "
+                         "square sizes: the dense FP8 rate this chip sustains outside attention")
     args = ap.parse_args()
+    if args.gemm_ceiling:
+        res = []
+        for n in (8192, 16384, 32768):
+            a = torch.randn(n, n, device="cuda").to(torch.float8_e4m3fn)
+            bt = torch.randn(n, n, device="cuda").to(torch.float8_e4m3fn)
+            one = torch.ones((), device="cuda", dtype=torch.float32)
+            f = lambda: torch._scaled_mm(a, bt.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+            ms, _ = timed_calls(f, max(args.steps, 10), max(args.warmup, 3))
+            tf = 2.0 * n ** 3 / ms / 1e9
+            res.append({"M": n, "N": n, "K": n, "ms": round(ms, 4), "tflops": round(tf, 1),
+                        "frac_of_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)})
+            del a, bt
+        print(json.dumps({"fp8_gemm_ceiling": res}))
+        return
     if args.copy_calibration:
         n = args.copy_calibration << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
