@@ -80,6 +80,22 @@ def timed_calls(fn, steps, warmup):
     return float(np.mean([a.elapsed_time(b) for a, b in ev])), wall
 
 
+def gemm_ceiling(n, steps, warmup):
+    """The vendor library's FP8 GEMM (torch._scaled_mm: OCP E4M3 operands,
+    unit scales, bf16 output) at M = N = K = n: the dense FP8 rate the chip
+    sustains under its own power limit, as a same-box reference."""
+    a = torch.randn(n, n, device="cuda").to(torch.float8_e4m3fn)
+    bt = torch.randn(n, n, device="cuda").to(torch.float8_e4m3fn)
+    one = torch.ones((), device="cuda", dtype=torch.float32)
+    ms, _ = timed_calls(lambda: torch._scaled_mm(a, bt.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16),
+                        steps, warmup)
+    del a, bt
+    torch.cuda.empty_cache()
+    tf = 2.0 * n ** 3 / ms / 1e9
+    return {"M": n, "N": n, "K": n, "ms": round(ms, 4), "tflops": round(tf, 1),
+            "frac_of_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)}
+
+
 def interleaved_calls(fns, rounds, warmup):
     """Median ms per call of each function (HIP events on the current
     stream), the functions called round-robin so that a drift of the board's
@@ -176,17 +192,7 @@ def main():
                          "square sizes: the dense FP8 rate this chip sustains outside attention")
     args = ap.parse_args()
     if args.gemm_ceiling:
-        res = []
-        for n in (8192, 16384, 32768):
-            a = torch.randn(n, n, device="cuda").to(torch.float8_e4m3fn)
-            bt = torch.randn(n, n, device="cuda").to(torch.float8_e4m3fn)
-            one = torch.ones((), device="cuda", dtype=torch.float32)
-            f = lambda: torch._scaled_mm(a, bt.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
-            ms, _ = timed_calls(f, max(args.steps, 10), max(args.warmup, 3))
-            tf = 2.0 * n ** 3 / ms / 1e9
-            res.append({"M": n, "N": n, "K": n, "ms": round(ms, 4), "tflops": round(tf, 1),
-                        "frac_of_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)})
-            del a, bt
+        res = [gemm_ceiling(n, max(args.steps, 10), max(args.warmup, 3)) for n in (8192, 16384, 32768)]
         print(json.dumps({"fp8_gemm_ceiling": res}))
         return
     if args.copy_calibration:
@@ -305,6 +311,7 @@ def main():
     in_bytes = 3 * 2 * w.B * w.S * w.H * 128
     prep_bytes = in_bytes + in_bytes // 2 + (in_bytes // 3)   # read q,k,v + V again; write 3 FP8 tensors
     sdpa = {} if args.no_comparator else bf16_comparator(q, k, v, max(2, min(args.steps, 3)))
+    gemm = None if args.no_comparator else gemm_ceiling(32768, 5, 2)
     sdpa_best = min(sdpa, key=sdpa.get) if sdpa else None
     sdpa_ms = sdpa[sdpa_best] if sdpa else None
 
@@ -338,6 +345,8 @@ def main():
         "cpu_baseline": None if cpu is None else {k_: cpu[k_] for k_ in ("value", "unit", "cores", "kind", "sample")},
         "kernel_ms": round(k_ms, 4),
         "kernel_tflops": round(kernel_tflops, 2),
+        "fp8_gemm_ceiling": gemm,
+        "kernel_frac_of_fp8_gemm_ceiling": None if gemm is None else round(kernel_tflops / gemm["tflops"], 4),
         "kernel_repair_ms": round(kr_ms, 4),
         "kernel_exp_fp8_ms": round(ke_ms, 4),
         "expcast_speedup_vs_exp_fp8": round(ke_ms / k_ms, 3),
