@@ -46,9 +46,10 @@
  *
  * Ownership: the caller allocates and owns q, k, v, out and the workspace
  * (device memory). The library never allocates or frees device memory in
- * these calls. A plan owns only host state: the descriptor, its sizes, and a
- * cached hipGraphExec of the prepare step, keyed on the pointers it was
- * captured with. A plan is used from one host thread at a time.
+ * these calls. A plan owns only host state: the descriptor, its sizes, and,
+ * when OC_ATTN_GRAPH=1 is set, a cached hipGraphExec of the prepare step,
+ * keyed on the pointers it was captured with. A plan is used from one host
+ * thread at a time.
  *
  * Execution: every call enqueues work on `stream` (a hipStream_t; NULL is the
  * default stream) and returns without synchronizing. Inputs are never
@@ -199,8 +200,12 @@ oc_status oc_attn_workspace_layout(const oc_attn_plan* plan, oc_attn_ws_layout* 
  * per-head V scale and codes packed transposed for the matrix cores (Open VC
  * Attention product page, kernel paragraph: per-block Q/K and per-head V
  * scales; the call quantizes to FP8 itself, API paragraph). The prepare
- * kernels run as one captured hipGraph (Open-VC news, "Архитектурные
- * оптимизации": Q/K/V preparation fused into one graph).
+ * kernels (two, or up to five with repair or K-mean smoothing) are launched
+ * back to back on `stream`; with OC_ATTN_GRAPH=1 in the environment they run
+ * instead as one captured hipGraph, replayed on later calls with the same
+ * pointers (Open-VC news, "Архитектурные оптимизации": Q/K/V preparation
+ * fused into one graph). On MI355X the direct launches cost less: the graph
+ * launch adds about 15 us.
  * q, k, v: device, [B,S,H,128] bf16/fp16 with the plan's strides; ws: device,
  * at least oc_attn_workspace_size bytes, 256-byte aligned, overwritten;
  * stream: hipStream_t. Errors as listed at the top of this file. */

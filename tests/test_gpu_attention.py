@@ -229,14 +229,27 @@ def test_softmax_scale_argument():
     assert oracle.rel_l2(out_rows(out, 0, 0, np.arange(400)), r["out"]) <= TOL
 
 
-def test_deterministic_and_graph_replays():
-    """The prepare graph is replayed on every call; eager work in between must
-    not disturb it and every replay must give the same bits."""
+@pytest.fixture
+def prepare_graph(request, monkeypatch):
+    """OC_ATTN_GRAPH for the test (read by the library on every prepare)."""
+    if request.param:
+        monkeypatch.setenv("OC_ATTN_GRAPH", "1")
+    else:
+        monkeypatch.delenv("OC_ATTN_GRAPH", raising=False)
+    return request.param
+
+
+@pytest.mark.parametrize("prepare_graph", [False, True], indirect=True)
+def test_deterministic_and_graph_replays(prepare_graph, monkeypatch):
+    """Repeated calls give the same bits, with eager work in between; with
+    the prepare graph (OC_ATTN_GRAPH=1) every call after the first replays it,
+    and new pointers re-capture it. The direct launches and the graph give
+    the same bits."""
     oc = _oc()
     q, k, v = workloads.make_inputs("s8192_h8", device="cuda", S=4096, H=4)
     ref = oc.attention(q, k, v).clone()
     for i in range(4):
-        junk = torch.randn(1 << 20, device="cuda").sum()      # eager work between replays
+        junk = torch.randn(1 << 20, device="cuda").sum()      # eager work between calls
         out = oc.attention(q, k, v)                            # same pointers: graph replay
         torch.cuda.synchronize()
         assert torch.equal(out, ref), i
@@ -248,6 +261,13 @@ def test_deterministic_and_graph_replays():
     o2 = oc.attention_prepared(prep)
     torch.cuda.synchronize()
     assert torch.equal(o2, ref)
+    rep = oc.attention_v_repair(q, k, v, 0.01).clone()
+    for i in range(3):
+        assert torch.equal(oc.attention_v_repair(q, k, v, 0.01), rep), i
+    if prepare_graph:
+        monkeypatch.delenv("OC_ATTN_GRAPH")
+        assert torch.equal(oc.attention(q, k, v), ref)             # direct launches, same bits
+        assert torch.equal(oc.attention_v_repair(q, k, v, 0.01), rep)
 
 
 def test_traversal_orders_match_their_oracle():
