@@ -108,3 +108,31 @@ def test_prepare_tiny_blocks_take_the_unit_scale():
     # head 1's values all count as zero: its output is zero
     assert torch.isfinite(out.float()).all()
     assert not out[0, :, 1].float().abs().max().item()
+
+
+def test_prepare_fp16_extremes():
+    """fp16 inputs at the ends of their range: values up to 65504, blocks of
+    fp16 subnormals (down to 2^-24), exact zeros and a head of V made of
+    subnormals only. Codes and scales bit-exact; the output finite and within
+    the usual tolerance of the oracle."""
+    import bit_fp8_attention_block_amd as oc
+    from gpu_util import compare
+    log("[prepare] fp16 extremes")
+    S, H = 700, 2
+    g = torch.Generator().manual_seed(21)
+    x = torch.randn(1, S, H, 128, generator=g)
+    q = (x * 20000.0).clamp(-65504, 65504)
+    q[0, 3, 0, 7] = 65504.0                                   # the largest finite fp16
+    k = x.flip(1) * 3.0
+    k[:, 128:256] = torch.randint(-1023, 1024, (1, 128, H, 128), generator=g).float() * 2.0 ** -24  # subnormals
+    k[:, 256:384, 1] = 0.0
+    v = torch.randn(1, S, H, 128, generator=g)
+    v[:, :, 1] = torch.randint(-1023, 1024, (1, S, 128), generator=g).float() * 2.0 ** -24          # head 1: subnormal V
+    q, k, v = (t.to(torch.float16).cuda() for t in (q, k, v))
+    assert torch.isfinite(q.float()).all() and (k[:, 128:256].float().abs().max() < 2.0 ** -14)
+    prep = oc.prepare(q, k, v)
+    out = oc.attention(q, k, v)
+    torch.cuda.synchronize()
+    _check_prepared(q, k, v, prep)
+    assert torch.isfinite(out.float()).all()
+    compare(q, k, v, out, [(0, 0), (0, 1)], np.arange(S), label="fp16 extremes", prep=prep)
