@@ -344,7 +344,8 @@ def key_tile_order(n_tiles: int) -> list:
 
 
 def expcast_attention_online(q, k, v, tau=None, rows=None, budget=0.0, ph=None, order="mid", chunk=256,
-                             m_trace=None, weights="expcast", k_smooth=False, v_smooth=False):
+                             m_trace=None, weights="expcast", k_smooth=False, v_smooth=False, code_trace=None,
+                             rcode_trace=None):
     """Single-pass (flash) form of ExpCast attention, as the pages' kernel runs
     it: keys are consumed in 128-key tiles in `order` ("mid" = key_tile_order,
     "ascending" = 0, 1, 2, ...). Per row, a running bit-aligned max M is raised
@@ -362,6 +363,13 @@ def expcast_attention_online(q, k, v, tau=None, rows=None, budget=0.0, ph=None, 
     one computed here (to replay another implementation's max decisions,
     which can differ where a tile's largest logit is within rounding of an
     integer). The rescale factors then follow from consecutive entries.
+
+    code_trace, if given, is an integer array [len(rows), S]: where an entry
+    is non-negative, that byte is used for (row, key) instead of the one
+    computed here; rcode_trace [len(rows), k] does the same for the repair
+    residuals' bytes. They replay another implementation's byte decisions at
+    entries whose exact value lies within that implementation's rounding of
+    a boundary between two codes (the caller checks that they do).
 
     weights="exp_cast" writes each tile's bytes by the path ExpCast replaces
     (exp_cast_codes against the same running max) instead; everything else
@@ -397,7 +405,11 @@ def expcast_attention_online(q, k, v, tau=None, rows=None, budget=0.0, ph=None, 
             else:
                 Mn = np.asarray(m_trace[c0:c0 + len(r), t], dtype=np.float64)
             f = np.where(np.isinf(M), 0.0, np.exp2(M - Mn))     # exact powers of two
-            P = VALUES[codes_of(xt, Mn)]
+            codes = codes_of(xt, Mn)
+            if code_trace is not None:
+                ct = np.asarray(code_trace[c0:c0 + len(r), ks])
+                codes = np.where(ct >= 0, ct, codes).astype(np.uint8)
+            P = VALUES[codes]
             O = O * f[:, None] + P @ vd[ks]
             if ph.vmean is not None:
                 Omu = Omu * f[:, None] + P.sum(axis=1)[:, None] * ph.vmean[t][None, :]
@@ -408,7 +420,11 @@ def expcast_attention_online(q, k, v, tau=None, rows=None, budget=0.0, ph=None, 
         O += Omu
         if ph.repair is not None and ph.repair.k > 0:
             rp = ph.repair
-            P = VALUES[codes_of(x[:, rp.sel], M)]
+            codes = codes_of(x[:, rp.sel], M)
+            if rcode_trace is not None:
+                ct = np.asarray(rcode_trace[c0:c0 + len(r)])
+                codes = np.where(ct >= 0, ct, codes).astype(np.uint8)
+            P = VALUES[codes]
             O += float(rp.sr) * (P @ decode(rp.rc))
         out[c0:c0 + len(r)] = O / L[:, None]
         Ms[c0:c0 + len(r)] = M.astype(np.int64)

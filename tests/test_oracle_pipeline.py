@@ -494,3 +494,47 @@ def test_online_replays_a_max_trace():
     c = oracle.expcast_attention_online(qh, kh, vh, rows=rows, m_trace=a["m_trace"] + 1)
     assert oracle.rel_l2(c["out"], a["out"]) < 0.05
     np.testing.assert_array_equal(c["M"], a["M"] + 1)
+
+
+@pytest.mark.parametrize("weights", ["expcast", "exp_cast"])
+def test_online_replays_bytes(weights):
+    """code_trace / rcode_trace: all entries negative (or the form's own
+    bytes) reproduce it exactly; replacing single bytes gives, on a one-tile
+    sequence, the weighted mean written out directly with those bytes
+    (O = sv * (sum_j dec(c_j) v_j + sr * sum_sel dec(r_j) r_j) / sum_j dec(c_j))."""
+    S = 120
+    q, k, v = workloads.make_inputs("s8192_h8", S=S, H=1)
+    qh, kh, vh = (t[0, :, 0].double().numpy() for t in (q, k, v))
+    rows = np.arange(0, S, 7)
+    budget = 0.05
+    a = oracle.expcast_attention_online(qh, kh, vh, rows=rows, weights=weights, budget=budget)
+    ph = a["ph"]
+    k_sel = ph.repair.k
+    none = np.full((len(rows), S), -1)
+    b = oracle.expcast_attention_online(qh, kh, vh, rows=rows, weights=weights, ph=ph, code_trace=none,
+                                        rcode_trace=np.full((len(rows), k_sel), -1))
+    np.testing.assert_array_equal(a["out"], b["out"])
+    x = oracle.log2_logits(ph, rows, TAU)
+    M = oracle.bitaligned_row_max(x)
+    codes_of = oracle.expcast_codes if weights == "expcast" else oracle.exp_cast_codes
+    own = codes_of(x, M).astype(np.int64)
+    rown = codes_of(x[:, ph.repair.sel], M).astype(np.int64)
+    c = oracle.expcast_attention_online(qh, kh, vh, rows=rows, weights=weights, ph=ph, code_trace=own,
+                                        rcode_trace=rown)
+    np.testing.assert_array_equal(a["out"], c["out"])
+    # one byte per row moved by one code (the row's largest weight), and one repair byte
+    mod = own.copy()
+    j = np.argmax(x, axis=1)
+    mod[np.arange(len(rows)), j] -= 1
+    rmod = rown.copy()
+    rmod[:, 0] = np.minimum(rmod[:, 0] + 1, 126)
+    d = oracle.expcast_attention_online(qh, kh, vh, rows=rows, weights=weights, ph=ph,
+                                        code_trace=np.where(np.arange(S)[None, :] == j[:, None], mod, -1),
+                                        rcode_trace=np.where(np.arange(k_sel)[None, :] == 0, rmod, -1))
+    dec = lambda c_: np.array([_dec(int(z)) for z in np.ravel(c_)]).reshape(np.shape(c_))  # noqa: E731
+    vd = dec(ph.vc)
+    rd = dec(ph.repair.rc)
+    P, R = dec(mod), dec(rmod)
+    want = (float(ph.sv) * (P @ vd) + float(ph.repair.sr) * (R @ rd)) / P.sum(axis=1)[:, None]
+    np.testing.assert_allclose(d["out"], want, rtol=1e-12, atol=0)
+    assert oracle.rel_l2(d["out"], a["out"]) > 1e-3
