@@ -16,7 +16,7 @@ from test_gpu_attention import _compare
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 16
+N_CASES = 48
 
 
 def _case(seed):
