@@ -20,7 +20,7 @@ import torch
 import oracle
 import workloads
 from gpu_util import (KERNEL_WEIGHTS, TOL, _oc, check_max_trace, compare, head64, kernel_dump,  # noqa: F401
-                      log, logit_error_bound, oracle_rows, out_rows)
+                      log, logit_error_bound, oracle_rows, out_rows, validated_codes)
 
 pytestmark = pytest.mark.gpu
 
@@ -48,6 +48,8 @@ def check_bytes(q, k, v, prep, b, h, rows, out=None, weights="expcast", tau=None
     log(f"  {label} (b={b},h={h}) {len(rows)} rows: byte agreement {agree:.6f}, max diff {diff.max()}, "
         f"tie-broken rows {ties}")
     assert agree >= 0.999 and diff.max() <= 1, (agree, diff.max())
+    # and every differing byte is one a logit within the error bound gives
+    validated_codes(d.codes, x, Mk.astype(np.float64), bound, weights)
     Mfinal = d.m_used.max(axis=1)
     Mo = oracle.bitaligned_row_max(x)
     xmax = x.max(axis=1)
