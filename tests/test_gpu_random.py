@@ -27,7 +27,7 @@ def _case(seed):
         H=int(r.integers(1, 4)),
         fp16=bool(r.integers(0, 2)),
         layout=str(r.choice(["contiguous", "three_dim", "fused_qkv"])),
-        scale=float(r.choice([0.0, 0.05, 0.12])),
+        scale=float(r.choice([0.0, 0.05, 0.12, 0.3, 1.0])),
         budget=float(r.choice([0.0, 0.0, 0.01, 0.05])),
         weights=str(r.choice(["expcast", "expcast", "exp_fp8"])),
         k_smooth=bool(r.integers(0, 3) == 0),
