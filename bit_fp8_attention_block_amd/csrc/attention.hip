@@ -436,7 +436,7 @@ __device__ __forceinline__ void spread_pair(float v, float& v0, float& v1) {
 // 8*tau*log2(e)*sq/8 for the wave's 32 queries, which share one 128-query
 // scale block.
 template <bool DUMP, bool EXPP>
-__device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], float aq8, float skj, float& Mv,
+__device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], float (&b)[QBW], float aq8, float skj, float& Mv,
                                              float& Mr, int (&sb)[QBW], v4f (&O)[QBW][8], v4f (&L)[QBW],
                                              v4f (&C)[QBW], int j, bool masked, const AttnArgs& a, int g,
                                              const int (&dslot)[QBW]) {
@@ -496,10 +496,10 @@ __device__ __forceinline__ void expcast_tile(v4f (&S)[QBW][8], v8i (&P)[QBW], fl
     sb[0] = 127 + (int)e0;
     sb[1] = 127 + (int)e1;
     Mv = Mn;
+    // the FMA's addend per block, in every lane, follows the running max
+    // (ExpCast: a and b over 65535, for bytes_expcast's unorm16 conversion)
+    spread_pair(EXPP ? 8.0f - Mn : __builtin_fmaf(-8.0f / 65535.0f, Mn, EXPCAST_C / 65535.0f), b[0], b[1]);
   }
-  float b[QBW];   // the FMA's addend per block, in every lane
-  // (ExpCast: a and b over 65535, for bytes_expcast's unorm16 conversion)
-  spread_pair(EXPP ? 8.0f - Mn : __builtin_fmaf(-8.0f / 65535.0f, Mn, EXPCAST_C / 65535.0f), b[0], b[1]);
   // a/65535 is the same in every lane of the wave: it goes to an SGPR, so the
   // 64 FMAs of a tile read two VGPRs each instead of three. (The empty
   // statement hides that the value is uniform, which would let the compiler
@@ -656,6 +656,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   v4f O[QBW][8], L[QBW], S[QBW][8];
   v8i P[QBW];
   float Mv = -__builtin_inff();    // running max per block by row parity (see expcast_tile)
+  float bq[QBW] = {0.0f, 0.0f};    // the ExpCast FMA's addend for Mv (set when Mv first grows)
   v4f C[QBW];                      // V-Smooth: row sums of the current batch of sixteen tiles
   float Mr = 0.0f;                 // reference max of O and L, same layout
   int sb[QBW] = {127, 127};        // E8M0 scale of the P operand: 2^(M - Mr)
@@ -743,7 +744,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
     if (ld_mu) load_means(mofs + ((s + 2) & (MU_NBUF - 1)) * MU_SLOT, mu_of(ta2), voff_mu);
     const float skj = skp[j];
     if (!GB) {
-      expcast_tile<DUMP, EXPP>(S, P, aq8, skj, Mv, Mr, sb, O, L, C, j, j == last_masked, a, g, dslot);
+      expcast_tile<DUMP, EXPP>(S, P, bq, aq8, skj, Mv, Mr, sb, O, L, C, j, j == last_masked, a, g, dslot);
       if (VSMOOTH) vsmooth_tile(P, sb, C, l16 == (s & 15) ? 127 : 0, ones);
       pv_tile<!VSMOOTH, true, !DUMP>(vbuf + b0 * TILE_BYTES, P, sb, one, O, L, lane, ones, pre);
       if (VSMOOTH && ((s & 15) == 15 || s + 1 == nT)) {
@@ -766,7 +767,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
         ofence(O);
       }
       __builtin_amdgcn_s_setprio(0);
-      expcast_tile<DUMP, EXPP>(S, P, aq8, skj, Mv, Mr, sb, O, L, C, j, j == last_masked, a, g, dslot);
+      expcast_tile<DUMP, EXPP>(S, P, bq, aq8, skj, Mv, Mr, sb, O, L, C, j, j == last_masked, a, g, dslot);
       if (VSMOOTH) vsmooth_tile(P, sb, C, l16 == (s & 15) ? 127 : 0, ones);
       // K step s+1 and V step s have been in LDS since the last barrier: the
       // first operands of the next QK and PV arrive before the next one
