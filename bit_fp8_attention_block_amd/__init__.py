@@ -51,7 +51,7 @@ class Desc(ctypes.Structure):
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in ("qhat", "kpack", "vpack", "sq", "sk", "vamax", "sv", "energy", "sel",
                                                "kselpack", "rpack", "sksel", "sr", "kmean", "kpart", "vmu",
-                                               "total_bytes")] + \
+                                               "sched", "total_bytes")] + \
                [(n, ctypes.c_int32) for n in ("n_ktiles", "n_qtiles", "s_pad_q", "n_sel_max", "n_sel_tiles_max")]
 
 
@@ -304,7 +304,9 @@ def attention_noalloc(q, k, v, budget=0.0, softmax_scale=None, out=None, weights
 
 
 def attention_prepared(prep: Prepared, with_repair=None, out=None, weights="expcast"):
-    """Attention only, on a workspace filled by prepare / prepare_v_repair."""
+    """Attention only, on a workspace filled by prepare / prepare_v_repair.
+    The call writes the workspace's work-item counters, so calls on one
+    Prepared must be ordered (one stream, or synchronized streams)."""
     _set_weights(prep.plan, weights)
     if with_repair is None:
         with_repair = prep.budget is not None

@@ -594,8 +594,55 @@ __device__ __forceinline__ void wait_loads(bool all, bool ld_k, bool ld_v, bool 
 // in iteration s (K s+3, V s+2) may stay in flight until the end of
 // iteration s+1, which hides L2 misses; so K and V get four LDS buffers each
 // (128 KiB).
+// Work items are (b, h, 256-query tile), numbered b-major; XCD x (the
+// workgroups i with i % 8 == x) owns the contiguous range [x*per, x*per + n_x),
+// so the workgroups one XCD runs at a time share K/V tiles in its L2. Under
+// full load the XCDs do not run at one speed (their mean workgroup times
+// differ by up to 5%), and a fixed split ends with the slowest. So a range's
+// first s0 items go by workgroup index, and the rest are claimed at run time:
+// a claiming workgroup first takes the next item of its own XCD's range, and
+// once that is used up, the next item of the range with the most items left.
+// ctr[0..7] count the claims made on each range, ctr[8] the claiming
+// workgroups that are done claiming; the last of them sets all nine back to
+// zero, once no claim can follow.
+// Every item is run exactly once: claim k on range x returns k once, and a
+// workgroup gives up only once it has seen every range used up (counters only
+// grow within a launch, so a count at or past a range's size stays there);
+// with at least as many claiming workgroups as claimed items, none is left.
+__device__ inline int claim_item(uint32_t* ctr, int nwork, int per, int s0, int n_claim) {
+  const int x = blockIdx.x & 7;
+  // claimable items of range y; claims compare unsigned, so that no counter
+  // value can give an item outside the range
+  auto range_left = [&](int y) { return (uint32_t)max(min(per, nwork - y * per) - s0, 0); };
+  int item = -1;
+  uint32_t i = __hip_atomic_fetch_add(&ctr[x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (i < range_left(x)) item = x * per + s0 + (int)i;
+  uint32_t used_up = 1u << x;
+  while (item < 0) {
+    int best = -1;
+    uint32_t most = 0;
+    for (int k = 1; k < 8; ++k) {
+      const int y = (x + k) & 7;
+      if ((used_up >> y) & 1u) continue;
+      const uint32_t c = __hip_atomic_load(&ctr[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t n = range_left(y);
+      if (c < n && n - c > most) { most = n - c; best = y; }
+    }
+    if (best < 0) break;
+    i = __hip_atomic_fetch_add(&ctr[best], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (i < range_left(best)) item = best * per + s0 + (int)i;
+    else used_up |= 1u << best;
+  }
+  const uint32_t done = __hip_atomic_fetch_add(&ctr[8], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  if (done == (uint32_t)n_claim - 1u) {
+    for (int y = 0; y < 9; ++y) __hip_atomic_store(&ctr[y], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return item;
+}
+
 template <bool REPAIR, bool DUMP, bool EXPP, bool VSMOOTH>
 __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
+  __shared__ int claimed;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   uint8_t* const kbuf = smem;
   uint8_t* const vbuf = smem + NBUF * TILE_BYTES;
@@ -605,12 +652,19 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(AttnArgs a) {
   if (DUMP) {
     b = a.dump_b; h = a.dump_h; qt = blockIdx.x;
   } else {
-    // XCD-aware mapping: workgroup i runs on XCD i % 8; give each XCD a
-    // contiguous range of (b, h, query tile) work items
     const int nwork = a.B * a.H * a.nQT;
     const int per = (nwork + 7) >> 3;
-    const int w = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-    if (w >= nwork) return;
+    const int j = blockIdx.x >> 3;
+    int w;
+    if (j < a.sched_s0) {
+      w = (blockIdx.x & 7) * per + j;
+      if (w >= nwork) return;
+    } else {
+      if (threadIdx.x == 0) claimed = claim_item(a.sched, nwork, per, a.sched_s0, a.sched_n_claim);
+      __syncthreads();
+      w = claimed;
+      if (w < 0) return;
+    }
     qt = w % a.nQT;
     const int bh_ = w / a.nQT;
     h = bh_ % a.H;
@@ -940,9 +994,24 @@ static hipError_t launch_variant(const AttnArgs& a, bool repair, bool dump, dim3
   return repair ? launch_one<true, false, EXPP, VSMOOTH>(a, grid, st) : launch_one<false, false, EXPP, VSMOOTH>(a, grid, st);
 }
 
-hipError_t launch_attention(const AttnArgs& a, bool repair, bool dump, hipStream_t st) {
+hipError_t launch_attention(const AttnArgs& args, bool repair, bool dump, hipStream_t st) {
+  AttnArgs a = args;
   const int nwork = a.B * a.H * a.nQT;
-  const dim3 grid = dump ? dim3(a.nQT) : dim3(8 * ((nwork + 7) / 8));
+  const int per = (nwork + 7) / 8;
+  // Claiming pays for its atomics only when a CU runs many workgroups: at
+  // 16 or more per CU (256 CUs), the last eighth of every XCD range is
+  // claimed, by one and a half times as many workgroups, so that a faster
+  // XCD can run up to 6% more than its own range.
+  int per_xcd = per;
+  a.sched_s0 = per;
+  a.sched_n_claim = 0;
+  if (!dump && nwork >= 16 * 256) {
+    const int tail = per / 8, claimers = tail + tail / 2;
+    a.sched_s0 = per - tail;
+    a.sched_n_claim = 8 * claimers;
+    per_xcd = a.sched_s0 + claimers;
+  }
+  const dim3 grid = dump ? dim3(a.nQT) : dim3(8 * per_xcd);
   if (a.vmu != nullptr)
     return a.exp_path ? launch_variant<true, true>(a, repair, dump, grid, st)
                       : launch_variant<false, true>(a, repair, dump, grid, st);

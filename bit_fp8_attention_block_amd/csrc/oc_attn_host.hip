@@ -129,6 +129,7 @@ static void compute_layout(oc_attn_plan* p) {
   L.kmean = take(BH * HEAD_DIM * 4);
   L.kpart = take(BH * L.n_ktiles * (uint64_t)HEAD_DIM * 8);
   L.vmu = take(BH * L.n_ktiles * (uint64_t)HEAD_DIM * 2);
+  L.sched = take(SCHED_WORDS * 4);
   L.total_bytes = off;
 }
 
@@ -197,6 +198,7 @@ static PrepArgs prep_args(const oc_attn_plan* p, const void* q, const void* k, c
   a.sk = (float*)(base + L.sk);
   a.vamax = (float*)(base + L.vamax);
   a.sv = (float*)(base + L.sv);
+  a.sched = (uint32_t*)(base + L.sched);
   if (p->k_smooth) {
     a.kmean = (float*)(base + L.kmean);
     a.kpart = (double*)(base + L.kpart);
@@ -309,8 +311,9 @@ static oc_status run_prepare(oc_attn_plan* p, const void* q, const void* k, cons
   return OC_OK;
 }
 
-static oc_status run_attention(oc_attn_plan* p, const void* ws, void* out, int n_sel, hipStream_t st) {
-  const AttnArgs a = attn_args(p, ws, out, n_sel);
+static oc_status run_attention(oc_attn_plan* p, void* ws, void* out, int n_sel, hipStream_t st) {
+  AttnArgs a = attn_args(p, ws, out, n_sel);
+  a.sched = (uint32_t*)((uint8_t*)ws + p->L.sched);
   const hipError_t e = launch_attention(a, n_sel > 0, false, st);
   return e == hipSuccess ? OC_OK : hip_fail(e);
 }
@@ -516,7 +519,7 @@ static oc_status forward_v_repair_noalloc_impl(oc_attn_plan* p, const void* q, c
   return run_attention(p, ws, out, n_sel, (hipStream_t)stream);
 }
 
-static oc_status forward_prepared_impl(oc_attn_plan* p, const void* ws, size_t ws_bytes, void* out, int with_repair,
+static oc_status forward_prepared_impl(oc_attn_plan* p, void* ws, size_t ws_bytes, void* out, int with_repair,
                                    void* stream) {
   if (!p || !ws || ((uintptr_t)ws & 255u)) return OC_ERR_INVALID_ARGUMENT;
   if (ws_bytes < p->L.total_bytes) return OC_ERR_WORKSPACE_TOO_SMALL;
@@ -623,7 +626,7 @@ oc_status oc_attn_forward_v_repair_noalloc(oc_attn_plan* p, const void* q, const
   return logged("oc_attn_forward_v_repair_noalloc", p, forward_v_repair_noalloc_impl(p, q, k, v, budget, out, stream), budget);
 }
 
-oc_status oc_attn_forward_prepared(oc_attn_plan* p, const void* ws, size_t ws_bytes, void* out, int with_repair,
+oc_status oc_attn_forward_prepared(oc_attn_plan* p, void* ws, size_t ws_bytes, void* out, int with_repair,
                                    void* stream) {
   return logged("oc_attn_forward_prepared", p, forward_prepared_impl(p, ws, ws_bytes, out, with_repair, stream), -1.0);
 }

@@ -12,6 +12,7 @@ constexpr int HEAD_DIM = 128;
 constexpr int KTILE = 128;        // keys per tile = Q/K scale block
 constexpr int BQ = 256;           // queries per attention workgroup
 constexpr int TILE_BYTES = KTILE * HEAD_DIM;   // one FP8 tile: 16 KiB
+constexpr int SCHED_WORDS = 16;  // attention work-item counters: 8 XCD ranges, a claim count, padding
 
 // ExpCast constant: byte = rne(8*(x - M) + 120 + beta), beta = -0.35
 // (VC-Attention write-up, "ExpCast-FP8" section; 120 is the E4M3 byte of 256).

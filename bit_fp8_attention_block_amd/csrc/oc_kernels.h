@@ -34,6 +34,7 @@ struct PrepArgs {
   float* sksel;
   float* sr;                   // [B][H][2]
   int n_sel, n_sel_tiles;
+  uint32_t* sched;             // [SCHED_WORDS] attention work-item counters, zeroed here
 };
 
 struct AttnArgs {
@@ -63,6 +64,11 @@ struct AttnArgs {
   uint8_t* dump_rcodes;        // [n_dump][n_sel] repair-pass bytes (or nullptr)
   float* dump_out32;           // [n_dump][128] fp32 output before BF16 rounding (or nullptr)
   int dump_b, dump_h;
+  // work-item counters (the DUMP variant does not use them): zero at launch,
+  // left zero by a launch that runs to its end
+  uint32_t* sched;
+  int sched_s0;                // items of an XCD range taken by static index (set by launch_attention)
+  int sched_n_claim;           // workgroups that claim the rest (0: all static)
 };
 
 hipError_t launch_prepare(const PrepArgs& a, bool fp16, hipStream_t st);

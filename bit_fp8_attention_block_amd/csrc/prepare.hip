@@ -151,6 +151,8 @@ __global__ __launch_bounds__(256) void prep_qk_kernel(PrepArgs a) {
   const int bh = b * a.H + h;
   const bool kv = blk < a.nT;
   __shared__ float red[16];
+  // the attention kernel's work-item counters start at zero
+  if ((blk | h | b) == 0 && tid < SCHED_WORDS) a.sched[tid] = 0u;
 
   uint4 ql[4], qh[4], kl[4], kh[4], vl[4], vh[4];
   uint32_t mq = 0, mk = 0, mv = 0;

@@ -53,7 +53,11 @@
  *
  * Execution: every call enqueues work on `stream` (a hipStream_t; NULL is the
  * default stream) and returns without synchronizing. Inputs are never
- * modified. `out` must not overlap q, k, v or the workspace.
+ * modified. `out` must not overlap q, k, v or the workspace. Every call that
+ * takes a writable workspace writes to it, oc_attn_forward_prepared included
+ * (the attention kernel claims work items through counters kept there), so
+ * calls that share a workspace must not overlap: enqueue them on one stream,
+ * or order their streams.
  *
  * Errors: every call returns an oc_status. Arguments are validated before
  * anything is enqueued:
@@ -138,11 +142,17 @@ typedef struct oc_attn_desc {
  *   vmu    bf16 [B][H][n_ktiles][128] V block means (V-Smooth only; vpack then
  *                                     holds the codes of v - mean, and sv and
  *                                     vamax refer to those residuals)
+ *   sched  u32 [16]                   work-item counters of the attention
+ *                                     kernel on long inputs (at least 4096
+ *                                     (b, h, 256-query tile) items): every
+ *                                     prepare call zeroes them, and every
+ *                                     attention launch that runs to its end
+ *                                     leaves them zero again
  */
 typedef struct oc_attn_ws_layout {
   uint64_t qhat, kpack, vpack, sq, sk, vamax, sv;
   uint64_t energy, sel, kselpack, rpack, sksel, sr;
-  uint64_t kmean, kpart, vmu;
+  uint64_t kmean, kpart, vmu, sched;
   uint64_t total_bytes;
   int32_t n_ktiles, n_qtiles, s_pad_q, n_sel_max, n_sel_tiles_max;
 } oc_attn_ws_layout;
@@ -269,8 +279,10 @@ oc_status oc_attn_forward_v_repair_noalloc(oc_attn_plan* plan, const void* q, co
 /* Attention only, on a workspace this plan prepared earlier (kernel-alone
  * timing; the plan remembers its 64 most recently prepared workspaces).
  * with_repair != 0 requires the workspace to come from
- * oc_attn_prepare_v_repair; its repair set is then applied. */
-oc_status oc_attn_forward_prepared(oc_attn_plan* plan, const void* ws, size_t ws_bytes, void* out,
+ * oc_attn_prepare_v_repair; its repair set is then applied. The prepared
+ * tensors are only read; the work-item counters (`sched`) are written, so
+ * two calls on one workspace must not overlap. */
+oc_status oc_attn_forward_prepared(oc_attn_plan* plan, void* ws, size_t ws_bytes, void* out,
                                    int with_repair, void* stream);
 
 /* Parity aid: run the attention kernel on the prepared workspace for the

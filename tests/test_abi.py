@@ -87,6 +87,8 @@ def test_workspace_size_and_layout():
     assert L.kpack - L.qhat >= B * H * nQT * 256 * 128
     assert L.vpack - L.kpack >= B * H * nT * 16384
     assert L.total_bytes == n.value >= L.sr + B * H * 8
+    # the attention kernel's 16 work-item counters sit last, past the V-Smooth means
+    assert L.sched % 256 == 0 and L.sched >= L.vmu + B * H * nT * 128 * 2 and L.total_bytes >= L.sched + 64
     lib.oc_attn_plan_destroy(p)
     st, p = create(make_desc(B=B, S=S, H=H), 0.0)
     L0 = oc.WsLayout()
