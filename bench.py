@@ -141,6 +141,69 @@ def cpu_baseline(q, k, v, w, rows_n):
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16 MFMA
 
 
+def board_state_during(fn, calls):
+    """Socket power, the power cap and the GFX clock of every XCD, read
+    through amdsmi (read-only queries) every 20 ms while fn runs `calls`
+    times back to back, outside every timed region. Medians over the samples
+    after the first 0.2 s; None where amdsmi cannot be used."""
+    import threading
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+    except Exception as e:  # noqa: BLE001
+        log(f"[bench] amdsmi unavailable ({e}); no board readings")
+        return None
+    try:
+        handles = amdsmi.amdsmi_get_processor_handles()
+        h = None
+        if len(handles) == 1:
+            h = handles[0]
+        else:
+            bus = getattr(torch.cuda.get_device_properties(torch.cuda.current_device()), "pci_bus_id", None)
+            for c in handles:
+                if bus is not None and int(amdsmi.amdsmi_get_gpu_device_bdf(c).split(":")[1], 16) == bus:
+                    h = c
+        if h is None:
+            log("[bench] amdsmi: could not tell which GPU torch uses; no board readings")
+            return None
+        cap = amdsmi.amdsmi_get_power_cap_info(h).get("power_cap")
+        samples, stop = [], threading.Event()
+
+        def sample():
+            t0 = time.perf_counter()
+            while not stop.is_set():
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                samples.append((time.perf_counter() - t0, m.get("current_socket_power"), m.get("current_gfxclks")))
+                time.sleep(0.02)
+
+        th = threading.Thread(target=sample)
+        th.start()
+        for _ in range(calls):
+            fn()
+        torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        late = [x for x in samples if x[0] > 0.2]
+        power = [float(x[1]) for x in late if isinstance(x[1], (int, float))]
+        clks = [[c for c in x[2] if isinstance(c, int) and 0 < c < 10000] for x in late if isinstance(x[2], list)]
+        nx = min((len(c) for c in clks), default=0)
+        if not power or nx == 0:
+            return None
+        by_xcd = [float(np.median([c[i] for c in clks])) for i in range(nx)]
+        return {"socket_power_w": float(np.median(power)),
+                "power_cap_w": None if not isinstance(cap, (int, float)) else cap / 1e6,
+                "gfxclk_mhz_by_xcd": by_xcd, "gfxclk_mhz_mean": round(float(np.mean(by_xcd)), 1),
+                "samples": len(late)}
+    except Exception as e:  # noqa: BLE001
+        log(f"[bench] amdsmi readings failed ({e})")
+        return None
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:  # noqa: BLE001
+            pass
+
+
 def bf16_comparator(q, k, v, steps):
     """torch SDPA on BF16 [B,H,S,D] tensors, each fused backend timed on its
     own: the flash backend with torch's ROCm library preference set to
@@ -276,6 +339,9 @@ def main():
         "v_smooth": lambda: oc.attention_prepared(prep_vs, out=out),
     }, args.steps, args.warmup)
     k_ms, kr_ms, ke_ms, kvs_ms = km["plain"], km["repair"], km["exp_fp8"], km["v_smooth"]
+    # the board's power and clocks under the plain kernel (an untimed run of about a second)
+    board = board_state_during(lambda: oc.attention_prepared(prep, with_repair=False, out=out),
+                               max(4, int(1000.0 / max(k_ms, 1e-3))))
     del prep, prep_vs
 
     # full call (prepare graph + attention), the headline step
@@ -348,6 +414,11 @@ def main():
         "kernel_tflops": round(kernel_tflops, 2),
         "fp8_gemm_ceiling": gemm,
         "kernel_frac_of_fp8_gemm_ceiling": None if gemm is None else round(kernel_tflops / gemm["tflops"], 4),
+        # socket power against its cap and the clock of every XCD under the kernel; the 5.0 PFLOP/s peak
+        # assumes 2.4 GHz, so the kernel's fraction of the peak at the clock it ran at is given beside it
+        "board_under_kernel": board,
+        "kernel_frac_at_measured_clock": None if not board else
+        round(kernel_tflops / (FP8_PEAK_TFLOPS * board["gfxclk_mhz_mean"] / 2400.0), 4),
         "kernel_repair_ms": round(kr_ms, 4),
         "kernel_exp_fp8_ms": round(ke_ms, 4),
         "expcast_speedup_vs_exp_fp8": round(ke_ms / k_ms, 3),
