@@ -142,10 +142,12 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16 MFMA
 
 
 def board_state_during(fn, calls):
-    """Socket power, the power cap and the GFX clock of every XCD, read
-    through amdsmi (read-only queries) every 20 ms while fn runs `calls`
-    times back to back, outside every timed region. Medians over the samples
-    after the first 0.2 s; None where amdsmi cannot be used."""
+    """Socket power, the power cap and the GFX clock the board reports for
+    every XCD, read through amdsmi (read-only queries) every 20 ms while fn
+    runs `calls` times back to back, outside every timed region (medians over
+    the samples after the first 0.2 s), and the share of that time the power
+    limiter was engaged (the board's PPT residency counter against its
+    accumulation counter). None where amdsmi cannot be used."""
     import threading
     try:
         import amdsmi
@@ -176,6 +178,7 @@ def board_state_during(fn, calls):
                 samples.append((time.perf_counter() - t0, m.get("current_socket_power"), m.get("current_gfxclks")))
                 time.sleep(0.02)
 
+        m_start = amdsmi.amdsmi_get_gpu_metrics_info(h)
         th = threading.Thread(target=sample)
         th.start()
         for _ in range(calls):
@@ -183,6 +186,14 @@ def board_state_during(fn, calls):
         torch.cuda.synchronize()
         stop.set()
         th.join()
+        m_end = amdsmi.amdsmi_get_gpu_metrics_info(h)
+        ppt = None
+        try:
+            ticks = m_end["accumulation_counter"] - m_start["accumulation_counter"]
+            if ticks > 0:
+                ppt = round((m_end["ppt_residency_acc"] - m_start["ppt_residency_acc"]) / ticks, 3)
+        except (KeyError, TypeError):
+            pass
         late = [x for x in samples if x[0] > 0.2]
         power = [float(x[1]) for x in late if isinstance(x[1], (int, float))]
         clks = [[c for c in x[2] if isinstance(c, int) and 0 < c < 10000] for x in late if isinstance(x[2], list)]
@@ -193,7 +204,7 @@ def board_state_during(fn, calls):
         return {"socket_power_w": float(np.median(power)),
                 "power_cap_w": None if not isinstance(cap, (int, float)) else cap / 1e6,
                 "gfxclk_mhz_by_xcd": by_xcd, "gfxclk_mhz_mean": round(float(np.mean(by_xcd)), 1),
-                "samples": len(late)}
+                "power_limiter_engaged": ppt, "samples": len(late)}
     except Exception as e:  # noqa: BLE001
         log(f"[bench] amdsmi readings failed ({e})")
         return None
@@ -342,6 +353,8 @@ def main():
     # the board's power and clocks under the plain kernel (an untimed run of about a second)
     board = board_state_during(lambda: oc.attention_prepared(prep, with_repair=False, out=out),
                                max(4, int(1000.0 / max(k_ms, 1e-3))))
+    board_exp = board_state_during(lambda: oc.attention_prepared(prep, with_repair=False, out=out, weights="exp_fp8"),
+                                   max(4, int(1000.0 / max(ke_ms, 1e-3))))
     del prep, prep_vs
 
     # full call (prepare graph + attention), the headline step
@@ -414,13 +427,14 @@ def main():
         "kernel_tflops": round(kernel_tflops, 2),
         "fp8_gemm_ceiling": gemm,
         "kernel_frac_of_fp8_gemm_ceiling": None if gemm is None else round(kernel_tflops / gemm["tflops"], 4),
-        # socket power against its cap and the clock of every XCD under the kernel; the 5.0 PFLOP/s peak
-        # assumes 2.4 GHz, so the kernel's fraction of the peak at the clock it ran at is given beside it
+        # socket power against its cap and the clock the board reports for every XCD under the kernel; the
+        # 5.0 PFLOP/s peak assumes 2.4 GHz, so the kernel's fraction of the peak at the reported clock is given
         "board_under_kernel": board,
-        "kernel_frac_at_measured_clock": None if not board else
+        "kernel_frac_at_reported_clock": None if not board else
         round(kernel_tflops / (FP8_PEAK_TFLOPS * board["gfxclk_mhz_mean"] / 2400.0), 4),
         "kernel_repair_ms": round(kr_ms, 4),
         "kernel_exp_fp8_ms": round(ke_ms, 4),
+        "board_under_exp_fp8_kernel": board_exp,
         "expcast_speedup_vs_exp_fp8": round(ke_ms / k_ms, 3),
         "kernel_v_smooth_ms": round(kvs_ms, 4),
         "full_call_ms_events": round(full_ev_ms, 4),
