@@ -125,3 +125,34 @@ def test_claimed_items_in_every_kernel_variant(variant):
         {"weights": "exp_cast"}
     compare(q, k, v, out, [(b, h)], rows, prep=prep, label=f"{label} {variant} ({b},{h})", **ckw)
     assert np.isfinite(out[b, :, h].float().cpu().numpy()).all()
+
+
+def test_claiming_kernel_replays_in_a_graph():
+    """The attention call captured in a graph, on a shape whose items are
+    partly claimed at run time: the counters reset themselves at the end of
+    each launch, so every replay, with eager work between them, gives the
+    bits of the eager call and leaves the counters at zero."""
+    oc = _oc()
+    label, B, S, H = CASES[0]
+    q, k, v = workloads.random_qkv(B, S, H, seed=23, device="cuda")
+    prep = oc.prepare(q, k, v)
+    ref = run_twice(oc, prep)                       # eager calls (also configure the kernel before capture)
+    out = torch.full(prep.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        oc.attention_prepared(prep, out=out)        # warm-up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            oc.attention_prepared(prep, out=out)
+    torch.cuda.synchronize()
+    assert not counters(prep).any()
+    for i in range(3):
+        out.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device="cuda").sum()   # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), i
+        assert not counters(prep).any(), (i, counters(prep))
+        del junk
